@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for frame-aligned windowed attention.
+
+This module draws random tensors and nothing else: it holds none of the
+attention arithmetic, so both the HIP path and the fp64 oracle can take their
+inputs from it without sharing any of the method's code.
+
+The workloads stand in for the unpublished production data of the source page
+("HeyGen 与 Google Cloud：将 Avatar IV 部署到 TPU", news.xcc.im/article/5328,
+sections "Deleting the Mask" and "Unchaining the Softmax"): a chunk of F video
+frames of T tokens each, tokens frame-major, H heads of width d.
+
+Recipe (one independent stream per (batch, head), so any single head can be
+regenerated without drawing the others):
+  * generator: ``torch.Generator(device)`` seeded with ``head_seed(seed, b, h)``;
+  * draws, in this order, all float32:
+      q = N(0,1) [N, d];  e = N(0,1) [N, d];
+      c = 4 * N(0,1) [1, d]        (only when keys carry a shared mean);
+      v = N(0,1) [N, d];
+      p = randint(0, T) [F]        (only for a loose head);
+  * k = e + c  (or k = e);
+  * a loose head multiplies, in every frame g, the raw key at token g*T + p[g]
+    (shared mean included) by 20;
+  * finally q, k, v are cast to the config dtype (bf16 rounds to nearest even).
+The cast tensors are the inputs; the oracle upcasts exactly these values.
+
+The stream differs between a CPU and a GPU generator; a comparison always
+feeds one set of drawn values to both sides.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import torch
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    F: int            # frames in the chunk
+    T: int            # tokens per frame
+    H: int            # heads
+    d: int            # head width
+    dtype: str        # "bf16" or "f32"
+    window: int       # frames on each side of the query frame
+    ref_frame: int    # the global reference frame
+    shared_mean: bool  # keys = c + N(0,1) with one c ~ N(0, 4^2) per head
+    loose_period: int = 0   # head h is loose iff loose_period and h % loose_period == loose_phase
+    loose_phase: int = 0
+    B: int = 1
+
+    @property
+    def N(self) -> int:
+        return self.F * self.T
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def is_loose(self, h: int) -> bool:
+        return self.loose_period > 0 and h % self.loose_period == self.loose_phase
+
+    def with_(self, **kw) -> "Config":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Config(**d)
+
+
+# The five workloads: a tiny fp32 plumbing case, a small bf16 case whose frame
+# span (22x40 patches = 880 tokens) is not a multiple of 128, the 720p- and
+# 1080p-shaped super-resolution chunks (45x80 and 68x120 latent patch grids),
+# and the 720p shape with 40 heads of which one in fifty has a loose bound.
+CONFIGS = {
+    "tiny": Config("tiny", F=5, T=48, H=2, d=64, dtype="f32", window=1,
+                   ref_frame=0, shared_mean=False),
+    "small": Config("small", F=9, T=880, H=16, d=128, dtype="bf16", window=2,
+                    ref_frame=0, shared_mean=True),
+    "720p": Config("720p", F=13, T=3600, H=24, d=128, dtype="bf16", window=2,
+                   ref_frame=0, shared_mean=True),
+    "1080p": Config("1080p", F=9, T=8160, H=24, d=128, dtype="bf16", window=1,
+                    ref_frame=0, shared_mean=True),
+    "stress": Config("stress", F=13, T=3600, H=40, d=128, dtype="bf16",
+                     window=2, ref_frame=0, shared_mean=True, loose_period=50,
+                     loose_phase=7),
+}
+
+
+def head_seed(seed: int, b: int, h: int) -> int:
+    """Seed of the (b, h) stream: distinct for every seed < 2^20, b, h < 4096."""
+    return (seed << 24) + (b << 12) + h
+
+
+def make_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
+    """Draw one head's (q, k, v), each [N, d] in the config dtype."""
+    g = torch.Generator(device=device)
+    g.manual_seed(head_seed(seed, b, h))
+    N, d = cfg.N, cfg.d
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((N, d), **kw)
+    k = torch.randn((N, d), **kw)
+    if cfg.shared_mean:
+        k += 4.0 * torch.randn((1, d), **kw)
+    v = torch.randn((N, d), **kw)
+    if cfg.is_loose(h):
+        p = torch.randint(0, cfg.T, (cfg.F,), generator=g, device=device)
+        rows = torch.arange(cfg.F, device=device) * cfg.T + p
+        k[rows] *= 20.0
+    dt = cfg.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+def make_inputs(cfg: Config, seed: int = 0, device="cpu"):
+    """Draw Q, K, V of shape [B, H, N, d] (contiguous) in the config dtype."""
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    Q = torch.empty(shape, dtype=cfg.torch_dtype, device=device)
+    K = torch.empty_like(Q)
+    V = torch.empty_like(Q)
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            q, k, v = make_head(cfg, seed, b, h, device)
+            Q[b, h], K[b, h], V[b, h] = q, k, v
+    return Q, K, V
+
+
+def to_f64(t: torch.Tensor):
+    """Exact upcast of drawn values to a float64 numpy array on the host."""
+    return t.detach().to("cpu", torch.float64).numpy()

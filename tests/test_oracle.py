@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle to facts other than itself (CPU only).
+
+Each test ties an oracle function to a brute-force construction, a library
+routine, a closed form or an exact invariant. The source page ("HeyGen 与
+Google Cloud：将 Avatar IV 部署到 TPU", news.xcc.im/article/5328) prints no
+worked example, so the only stored values are the hand-derived slice sizes in
+tests/golden/.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fsa_oracle as orc
+from frame_aligned_block_amd.inputs import CONFIGS, make_head, make_inputs, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "slice_sizes.json")
+
+
+def golden_cases():
+    with open(GOLDEN) as fh:
+        return json.load(fh)["cases"]
+
+
+def dense_mask(F, T, window, ref_frame):
+    """N x N boolean mask built element by element from the definition:
+    key j is visible to query i iff the frames differ by at most the window,
+    or key j lies in the reference frame."""
+    fi = np.arange(F * T)[:, None] // T
+    fj = np.arange(F * T)[None, :] // T
+    return (np.abs(fi - fj) <= window) | (fj == ref_frame)
+
+
+def rand_qkv(rng, B, H, N, d, mean_scale=0.0):
+    Q = rng.standard_normal((B, H, N, d))
+    K = rng.standard_normal((B, H, N, d)) + mean_scale * rng.standard_normal((B, H, 1, d))
+    V = rng.standard_normal((B, H, N, d))
+    return Q, K, V
+
+
+# ---------------------------------------------------------------- slice / plan
+
+@pytest.mark.parametrize("case", golden_cases(), ids=lambda c: c["name"])
+def test_slice_sizes_match_hand_derivation(case):
+    F, w, r = case["F"], case["window"], case["ref_frame"]
+    sizes = [len(orc.slice_frames(F, w, r, f)) for f in range(F)]
+    assert sizes == case["slice_sizes"]
+    assert orc.valid_pairs_per_head(F, case["T"], w, r) == case["total"] * case["T"] ** 2
+
+
+@pytest.mark.parametrize("case", golden_cases(), ids=lambda c: c["name"])
+def test_plan_tile_count_closed_form(case):
+    F, T, w, r = case["F"], case["T"], case["window"], case["ref_frame"]
+    blocks = [b for b in range(16, T + 1, 16) if T % b == 0]
+    for bq in blocks[:3]:
+        for bk in blocks[-2:]:
+            p = orc.plan(F, T, w, r, bq, bk)
+            assert p["nnz"] == case["total"] * (T // bq) * (T // bk)
+
+
+@pytest.mark.parametrize("F,T,w,r,bq,bk", [
+    (5, 48, 1, 0, 16, 16), (5, 48, 1, 0, 48, 16), (5, 48, 1, 0, 16, 48),
+    (7, 32, 1, 3, 16, 32), (6, 48, 0, 5, 48, 48), (4, 16, 3, 2, 16, 16),
+    (9, 880, 2, 0, 80, 176), (9, 880, 2, 0, 880, 16),
+])
+def test_plan_matches_bruteforce_mask(F, T, w, r, bq, bk):
+    mask = dense_mask(F, T, w, r)
+    nqb, nkb = F * T // bq, F * T // bk
+    tiles = mask.reshape(nqb, bq, nkb, bk)
+    live = tiles.any(axis=(1, 3))
+    full = tiles.all(axis=(1, 3))
+    # frame alignment: a live tile is a full tile, never a partial one
+    assert np.array_equal(live, full)
+    p = orc.plan(F, T, w, r, bq, bk)
+    ref_rows, ref_cols = np.nonzero(live)          # row-major: (qb asc, kb asc)
+    assert np.array_equal(p["col_idx"], ref_cols)
+    assert np.array_equal(p["row_ptr"], np.concatenate([[0], np.cumsum(live.sum(axis=1))]))
+    assert np.array_equal(p["qframe"], np.arange(nqb) * bq // T)
+    # runs cover exactly the live key tokens of each q-block, in order
+    for qb in range(nqb):
+        toks = np.concatenate([np.arange(a, e) for a, e in p["runs"][qb]])
+        assert np.array_equal(toks, np.nonzero(mask[qb * bq])[0])
+        assert len(p["runs"][qb]) <= 2
+
+
+def test_plan_rejects_unaligned_blocks():
+    with pytest.raises(ValueError):
+        orc.plan(5, 48, 1, 0, 32, 16)       # 32 does not divide 48
+    with pytest.raises(ValueError):
+        orc.plan(5, 48, 1, 0, 24, 24)       # not a multiple of 16
+
+
+# ---------------------------------------------------------------- attention
+
+def loops_attention(Q, K, V, F, T, w, r, scale):
+    """Masked softmax attention by explicit scalar loops (math.exp)."""
+    N, d = Q.shape
+    out = np.zeros((N, d))
+    for i in range(N):
+        fi = i // T
+        js = [j for j in range(N) if abs(j // T - fi) <= w or j // T == r]
+        s = [scale * sum(Q[i, c] * K[j, c] for c in range(d)) for j in js]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        for c in range(d):
+            out[i, c] = sum(e[n] * V[js[n], c] for n in range(len(js))) / z
+    return out
+
+
+@pytest.mark.parametrize("F,T,w,r", [(4, 16, 1, 2), (5, 16, 0, 0), (3, 16, 1, 0)])
+def test_attention_matches_scalar_loops(F, T, w, r):
+    rng = np.random.default_rng(11)
+    d = 8
+    Q, K, V = rand_qkv(rng, 1, 1, F * T, d)
+    want = loops_attention(Q[0, 0], K[0, 0], V[0, 0], F, T, w, r, 0.37)
+    got = orc.attention(Q, K, V, F, T, w, r, 0.37)[0, 0]
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+@pytest.mark.parametrize("F,T,w,r", [(5, 48, 1, 0), (7, 32, 1, 3), (6, 16, 2, 5), (4, 48, 3, 1)])
+def test_attention_matches_torch_sdpa_with_mask(F, T, w, r):
+    rng = np.random.default_rng(5)
+    d = 64
+    Q, K, V = rand_qkv(rng, 1, 2, F * T, d, mean_scale=3.0)
+    scale = 1 / math.sqrt(d)
+    mask = torch.from_numpy(dense_mask(F, T, w, r))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+        attn_mask=mask, scale=scale).numpy()
+    got = orc.attention(Q, K, V, F, T, w, r, scale)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_full_window_is_dense_attention():
+    cfg = CONFIGS["tiny"]
+    Q, K, V = (to_f64(t) for t in make_inputs(cfg, seed=3))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+        scale=cfg.scale).numpy()
+    got = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.F - 1, 2, cfg.scale)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_attention_rows_matches_full():
+    cfg = CONFIGS["tiny"]
+    Q, K, V = (to_f64(t) for t in make_inputs(cfg))
+    full = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    rows = np.array([0, 47, 48, 100, 239, 150])
+    part = orc.attention_rows(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame,
+                              cfg.scale, 0, 1, rows)
+    assert np.max(np.abs(part - full[0, 1, rows])) < 1e-14
+
+
+def test_centring_invariance():
+    rng = np.random.default_rng(2)
+    F, T, w, r, d = 6, 32, 1, 0, 32
+    Q, K, V = rand_qkv(rng, 1, 2, F * T, d, mean_scale=4.0)
+    base = orc.attention(Q, K, V, F, T, w, r, 0.2)
+    mu = orc.key_mean(K)
+    centred = orc.attention(Q, K - mu[:, :, None, :], V, F, T, w, r, 0.2)
+    shifted = orc.attention(Q, K + rng.standard_normal((1, 2, 1, d)), V, F, T, w, r, 0.2)
+    assert np.max(np.abs(centred - base)) < 1e-12
+    assert np.max(np.abs(shifted - base)) < 1e-12
+
+
+def test_key_mean_closed_form():
+    # keys = c +/- a_j e_k in pairs: the mean is exactly c
+    d, c = 8, np.arange(1.0, 9.0)
+    dev = np.zeros((16, d))
+    for j in range(8):
+        dev[2 * j, j] = j + 0.5
+        dev[2 * j + 1, j] = -(j + 0.5)
+    K = (c + dev)[None, None]
+    assert np.allclose(orc.key_mean(K)[0, 0], c, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- bounds
+
+def test_bounds_hand_case():
+    """F=3 frames of T=16 tokens, d=4, window 0, reference frame 2.
+
+    Keys are mu + x_j with mu = (1, -2, 3, 0.5) and deviations x_j that cancel
+    over the chunk; frame g's largest deviation norm is 1, 5 and 2.
+    Slices: frame 0 -> {0, 2}, frame 1 -> {1, 2}, frame 2 -> {2}; so
+    R_S = (max(1,2), max(5,2), 2) = (2, 5, 2).
+    Queries: row 3 of frame 0 is (3, 4, 0, 0) (norm 5), row 16+7 is
+    (0, 0, 0, 2) (norm 2), row 32+1 is (1, 1, 1, 1) (norm 2); all other rows 0.
+    With scale 0.5 the row bounds are 0.5*5*2 = 5, 0.5*2*5 = 5, 0.5*2*2 = 2,
+    so stat = 5 (eligible); with scale 8 the stat is 80 (not eligible).
+    """
+    F, T, d = 3, 16, 4
+    mu = np.array([1.0, -2.0, 3.0, 0.5])
+    x = np.zeros((F * T, d))
+    x[0] = [1, 0, 0, 0]; x[1] = [-1, 0, 0, 0]           # frame 0: norm 1
+    x[16] = [0, 3, 4, 0]; x[17] = [0, -3, -4, 0]         # frame 1: norm 5
+    x[18] = [0, 1, 0, 0]; x[19] = [0, -1, 0, 0]
+    x[32] = [0, 0, 0, 2]; x[33] = [0, 0, 0, -2]          # frame 2: norm 2
+    Q = np.zeros((F * T, d))
+    Q[3] = [3, 4, 0, 0]; Q[23] = [0, 0, 0, 2]; Q[33] = [1, 1, 1, 1]
+    K = (mu + x)[None, None]
+    b = orc.bounds(Q[None, None], K, F, T, 0, 2, 0.5)
+    assert np.allclose(b["mu"][0, 0], mu, atol=1e-15)
+    assert np.allclose(b["R"][0, 0], [1, 5, 2], atol=1e-15)
+    assert np.allclose(b["R_S"][0, 0], [2, 5, 2], atol=1e-15)
+    assert np.allclose(b["qnorm"][0, 0, [3, 23, 33, 0]], [5, 2, 2, 0], atol=1e-15)
+    assert np.allclose(b["bound"][0, 0, [3, 23, 33]], [5, 5, 2], atol=1e-15)
+    assert b["stat"][0, 0] == pytest.approx(5.0, abs=1e-14)
+    assert bool(b["elig"][0, 0])
+    # the threshold is inclusive: the largest row bound is 10 * scale, and
+    # scale 3.2 gives exactly 32.0 in fp64 (3.2*5 and 6.4*5 round to 16, 32)
+    for scale, elig in [(2.0, True), (3.2, True), (3.25, False)]:
+        bs = orc.bounds(Q[None, None], K, F, T, 0, 2, scale)
+        assert bs["stat"][0, 0] == pytest.approx(10 * scale, abs=1e-12)
+        assert bool(bs["elig"][0, 0]) == elig, scale
+    b8 = orc.bounds(Q[None, None], K, F, T, 0, 2, 8.0)
+    assert b8["stat"][0, 0] == pytest.approx(80.0, abs=1e-12)
+    assert not bool(b8["elig"][0, 0])
+    # without centring the norms are those of the raw keys
+    raw = orc.bounds(Q[None, None], K, F, T, 0, 2, 0.5, centre=False)
+    assert np.allclose(raw["R"][0, 0], np.linalg.norm(K[0, 0], axis=1).reshape(F, T).max(1))
+
+
+def centred_logit_max(Q, K, F, T, w, r, scale, b, h, rows):
+    mu = K[b, h].mean(axis=0)
+    out = []
+    for i in rows:
+        keys = [j for j in range(F * T) if abs(j // T - i // T) <= w or j // T == r]
+        out.append((scale * ((K[b, h][keys] - mu) @ Q[b, h][i])).max())
+    return np.array(out)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_bound_is_at_least_the_true_row_max(name):
+    cfg = CONFIGS[name]
+    rng = np.random.default_rng(1)
+    q, k, v = make_head(cfg, 0, 0, 0)
+    Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+    bnd = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    rows = np.arange(cfg.N) if name == "tiny" else rng.choice(cfg.N, 300, replace=False)
+    m = centred_logit_max(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0, 0, rows)
+    assert np.all(bnd["bound"][0, 0, rows] >= m)
+    # and the bound is not vacuous: the gap stays well below the bound itself
+    assert np.median(bnd["bound"][0, 0, rows] - m) < np.median(bnd["bound"][0, 0, rows])
+
+
+def test_bound_is_attained_when_query_parallel_to_the_longest_key():
+    rng = np.random.default_rng(4)
+    F, T, d = 3, 16, 16
+    Q, K, _ = rand_qkv(rng, 1, 1, F * T, d, mean_scale=2.0)
+    kc = K[0, 0] - K[0, 0].mean(axis=0)
+    j = int(np.argmax(np.linalg.norm(kc, axis=1)))
+    Q[0, 0, 5] = 0.7 * kc[j]                        # row 5 sits in frame 0
+    bnd = orc.bounds(Q, K, F, T, 2, 0, 0.25)       # window covers every frame
+    s = 0.25 * (kc @ Q[0, 0, 5])
+    assert bnd["bound"][0, 0, 5] == pytest.approx(s.max(), rel=1e-14)
+
+
+def test_eligibility_by_construction_on_full_size_heads():
+    """Normal heads of the full-size configs are eligible with a margin; the
+    stress config's loose head (h % 50 == 7) is not; without centring the
+    normal heads would not be eligible (centring tightens the bound)."""
+    margin = 1.05
+    for name, h in [("720p", 0), ("1080p", 3), ("stress", 6), ("stress", 7)]:
+        cfg = CONFIGS[name]
+        q, k, _ = make_head(cfg, 0, 0, h)
+        Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+        b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        stat = b["stat"][0, 0]
+        if cfg.is_loose(h):
+            assert stat > orc.BETA * margin, (name, h, stat)
+            assert not bool(b["elig"][0, 0])
+        else:
+            assert stat < orc.BETA / margin, (name, h, stat)
+            assert bool(b["elig"][0, 0])
+            raw = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame,
+                             cfg.scale, centre=False)
+            assert raw["stat"][0, 0] > orc.BETA * margin, (name, h, raw["stat"])
+
+
+# ---------------------------------------------------------------- routes
+
+def test_fixed_max_and_online_routes_equal_the_definition():
+    cfg = CONFIGS["small"]
+    q, k, v = make_head(cfg, 0, 0, 5)
+    Q, K, V = (to_f64(t)[None, None] for t in (q, k, v))
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(cfg.N, 40, replace=False))
+    args = (Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0, 0, rows)
+    want = orc.attention_rows(*args)
+    assert np.max(np.abs(orc.attention_fixed_max(*args) - want)) < 1e-12
+    assert np.max(np.abs(orc.attention_online(*args, block=80) - want)) < 1e-12
+    assert np.max(np.abs(orc.attention_online(*args, block=16, centre=False) - want)) < 1e-12
+
+
+def test_two_pass_merge_equals_single_pass_and_pins_no_double_count():
+    F, T, w, d = 7, 16, 1, 16
+    rng = np.random.default_rng(8)
+    Q, K, V = rand_qkv(rng, 1, 1, F * T, d)
+    r = 3
+    rows = np.arange(F * T)
+    want = orc.attention_rows(Q, K, V, F, T, w, r, 0.3, 0, 0, rows)
+    got = orc.attention_two_pass(Q, K, V, F, T, w, r, 0.3, 0, 0, rows)
+    assert np.max(np.abs(got - want)) < 1e-12
+    # rows of frames 2..4 hold the reference frame in their window already:
+    inside = rows[(rows // T >= 2) & (rows // T <= 4)]
+    dbl = orc.attention_two_pass(Q, K, V, F, T, w, r, 0.3, 0, 0, inside, add_ref_always=True)
+    assert np.min(np.max(np.abs(dbl - want[inside]), axis=1)) > 1e-6
+
+
+# ---------------------------------------------------------------- probes
+
+def test_structured_value_probes():
+    F, T, w, r, d = 6, 32, 1, 4, 16
+    N = F * T
+    rng = np.random.default_rng(6)
+    Q, K, _ = rand_qkv(rng, 1, 1, N, d, mean_scale=2.0)
+    frame = np.arange(N) // T
+    # (i) one-hot frame values: weight lands only on the slice's frames
+    V1 = np.zeros((1, 1, N, d))
+    V1[0, 0, np.arange(N), frame] = 1.0
+    O = orc.attention(Q, K, V1, F, T, w, r, 0.5)[0, 0]
+    for i in range(N):
+        allowed = {g for g in range(F) if abs(g - i // T) <= w} | {r}
+        for g in range(F):
+            if g not in allowed:
+                assert O[i, g] == 0.0
+        assert abs(O[i, :F].sum() - 1.0) < 1e-12
+    # (ii) one-hot 16-key granule values: every granule of the slice gets weight
+    V2 = np.zeros((1, 1, N, d))
+    V2[0, 0, np.arange(N), (np.arange(N) // 16) % d] = 1.0
+    O2 = orc.attention(Q, K, V2, F, T, w, r, 0.5)[0, 0]
+    assert np.all(np.abs(O2.sum(axis=1) - 1.0) < 1e-12)
+    # (iii) constant values pass through exactly
+    O3 = orc.attention(Q, K, np.ones((1, 1, N, d)), F, T, w, r, 0.5)
+    assert np.max(np.abs(O3 - 1.0)) < 1e-14
+    # (iv) zero queries give the plain mean of the slice's values
+    V4 = rng.standard_normal((1, 1, N, d))
+    O4 = orc.attention(np.zeros((1, 1, N, d)), K, V4, F, T, w, r, 0.5)[0, 0]
+    for f in range(F):
+        sel = (np.abs(frame - f) <= w) | (frame == r)
+        want = V4[0, 0][sel].mean(axis=0)
+        assert np.max(np.abs(O4[f * T:(f + 1) * T] - want)) < 1e-13
