@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of frame-aligned windowed attention on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input,
+already resident in HBM: fsa_bounds (key mean, centred keys, norms,
+eligibility) then fsa_forward (the attention), through the C ABI, on torch's
+current stream. The tile plan is built once per shape before timing.
+
+Workload (default): the 720p-shaped super-resolution chunk, 13 frames of
+3600 tokens (a 45x80 latent patch grid), 24 heads of width 128, bf16, each
+frame attending to frames within +-2 plus reference frame 0; inputs drawn by
+frame_aligned_block_amd.inputs with seed 0.
+
+Prints one JSON line. value = valid-tile TFLOP/s of the whole step, with
+valid FLOPs = 4 * d * (valid query-key pairs) * B * H (Q.K^T and P.V on live
+tiles only). roofline.achieved = the same FLOPs / the forward kernel's mean
+launch time, from HIP events recorded on the launch stream around each
+forward launch inside the timed loop.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 720p]
+    python bench.py --calibrate-copy BYTES   # a plain copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 4096 bf16 FLOP/clk x 2.4 GHz (dense)
+PEAK_FP32_TFLOPS = 157.3      # fp32 vector
+METRIC = "valid-tile TFLOP/s and % bf16 MFMA peak, ms/call, 720p-shaped SR attention"
+FWD_SOURCES = ("frame_aligned_block_amd/csrc/forward.hip",
+               "frame_aligned_block_amd/csrc/fsa_internal.h",
+               "frame_aligned_block_amd/csrc/plan.cpp")
+PMC_SUMMARY = "profiles/fsa_forward_720p_pmc.txt"
+
+
+def forward_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per forward launch from the committed counter summary, or
+    None when it is missing, for another workload, or taken on other code."""
+    path = os.path.join(ROOT, PMC_SUMMARY)
+    if config != "720p" or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"^source_sha256:\s*(\w+)", text, re.M)
+    tb = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not src or not tb or src.group(1) != forward_source_hash():
+        return None
+    return float(tb.group(1))
+
+
+def cpu_baseline(cfg, Q, K, V, seconds: float):
+    """The fp64 oracle, as it stands, on whole (head, frame) blocks of the
+    same workload until about `seconds` of CPU work; valid TFLOP/s."""
+    import numpy as np
+    from oracle import fsa_oracle as orc
+    from frame_aligned_block_amd.inputs import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"]
+                      or [1])
+    except Exception:   # noqa: BLE001
+        threads = 1
+    # heaviest frames first, cycling over heads
+    frames = sorted(range(cfg.F), key=lambda f: -len(orc.slice_frames(cfg.F, cfg.window,
+                                                                       cfg.ref_frame, f)))
+    units = [(h, f) for f in frames for h in range(cfg.H)]
+    cache = {}
+    flops = 0.0
+    spent = 0.0
+    n = 0
+    for h, f in units:
+        if spent >= seconds:
+            break
+        if h not in cache:
+            cache.clear()
+            cache[h] = tuple(to_f64(t[0, h])[None, None] for t in (Q, K, V))
+        q, k, v = cache[h]
+        rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
+        t0 = time.perf_counter()
+        orc.attention_rows(q, k, v, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0, 0,
+                           rows)
+        spent += time.perf_counter() - t0
+        flops += 4.0 * cfg.d * cfg.T * cfg.T * len(orc.slice_frames(cfg.F, cfg.window,
+                                                                    cfg.ref_frame, f))
+        n += 1
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} (head, query-frame) blocks of {cfg.T} rows each of the {cfg.name} "
+                      f"workload (heaviest frames first), {flops / 1e9:.0f} valid GFLOP in "
+                      f"{spent:.1f} s; fp64 numpy, BLAS on {threads} threads"}
+
+
+def calibrate_copy(nbytes: int) -> None:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 5}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p")
+    ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed"])
+    ap.add_argument("--ab-launches", type=int, default=5,
+                    help="timed online-only forward launches for the A/B figure")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bq", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the path shards by head across GPUs, which is not built here)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return 0
+
+    from frame_aligned_block_amd import fsa
+    from frame_aligned_block_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    print(f"[bench] {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
+    Q, K, V = make_inputs(cfg, seed=0, device="cuda")
+    code = fsa.FSA_BF16 if cfg.dtype == "bf16" else fsa.FSA_F32
+    plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
+                                              cfg.ref_frame, args.bq, 0, code))
+    ws = torch.zeros(fsa.fsa_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(Q)
+    pairs = fsa.fsa_plan_valid_pairs(plan)
+    flops = 4.0 * cfg.d * pairs * cfg.B * cfg.H
+    stream = torch.cuda.current_stream()
+
+    def step(mode=args.mode):
+        fsa.fsa_bounds(plan, Q, K, ws, cfg.scale, stream)
+        fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, mode, stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fsa.fsa_bounds(plan, Q, K, ws, cfg.scale, stream)
+        ev[i][1].record(stream)
+        fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, args.mode, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    bnd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    # A/B: the same forward with every head on the online path
+    ab = None
+    if args.ab_launches > 0 and args.mode != "online":
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(args.ab_launches + 1)]
+        fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, "online", stream)
+        e[0].record(stream)
+        for i in range(args.ab_launches):
+            fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, "online", stream)
+            e[i + 1].record(stream)
+        torch.cuda.synchronize()
+        on_ms = e[0].elapsed_time(e[-1]) / args.ab_launches
+        step()                          # leave O as the benchmarked mode wrote it
+        torch.cuda.synchronize()
+        ab = {"online_only_forward_ms": round(on_ms, 4),
+              "online_only_forward_tflops": round(flops / on_ms / 1e9, 2),
+              "fixed_max_speedup": round(on_ms / fwd_ms, 4)}
+
+    elig = fsa.workspace_views(plan, ws)["elig"].float().mean().item()
+    bf16 = cfg.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    achieved = flops / fwd_ms / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(flops / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-shaped SR chunk: F={cfg.F} frames x T={cfg.T} "
+                               f"tokens ({cfg.N} tokens), H={cfg.H}, d={cfg.d}, {cfg.dtype}, "
+                               f"window +-{cfg.window} + reference frame {cfg.ref_frame}",
+                   "B": cfg.B, "H": cfg.H, "F": cfg.F, "T": cfg.T, "d": cfg.d,
+                   "mode": args.mode, "bq": fsa.fsa_plan_shape(plan).bq,
+                   "valid_pairs_per_head": pairs, "valid_flops_per_step": flops},
+        "ms_per_call": round(ms_step, 4),
+        "pct_bf16_peak": round(100.0 * flops / ms_step / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "forward_ms": round(fwd_ms, 4),
+        "bounds_ms": round(bnd_ms, 4),
+        "eligible_head_fraction": round(elig, 4),
+        "ab": ab,
+        "roofline": {"kernel": "fwd_bf16" if bf16 else "fwd_f32",
+                     "bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(cfg.name)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,60 @@
+"""Build libfsa.so (gfx950) in-tree with hipcc.
+
+    python -m frame_aligned_block_amd.build [--verbose]
+
+Compiles every source under csrc/ into frame_aligned_block_amd/libfsa.so.
+HIP code is built with packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfsa.so")
+SOURCES = ["plan.cpp", "abi.cpp", "bounds.hip", "forward.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def command(out: str = LIB, extra=()) -> list[str]:
+    srcs = []
+    for s in SOURCES:
+        path = os.path.join(CSRC, s)
+        # host-only sources are still compiled by the HIP driver, as HIP
+        srcs += ["-x", "hip", path]
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument",
+            "-I", INCLUDE, *extra, *srcs, "-o", out]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp, extra)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

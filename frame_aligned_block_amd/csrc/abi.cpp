@@ -1,0 +1,217 @@
+// C-ABI layer of libfsa: argument validation, error reporting, and the
+// per-shape plan cache behind fsa_attention. Kernels live in bounds.hip and
+// forward.hip; the plan builder in plan.cpp.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+}
+
+}  // namespace fsa
+
+using fsa::set_error;
+
+namespace {
+
+bool good_scale(float scale) { return std::isfinite(scale) && scale > 0.0f; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t tensor_bytes(const fsa_plan& p) {
+    const fsa_shape& s = p.shape;
+    return size_t(s.B) * s.H * s.F * s.T * s.d * (s.dtype == FSA_BF16 ? 2 : 4);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" const char* fsa_status_string(fsa_status st) {
+    switch (st) {
+        case FSA_OK: return "FSA_OK";
+        case FSA_ERR_INVALID_ARG: return "FSA_ERR_INVALID_ARG";
+        case FSA_ERR_UNSUPPORTED: return "FSA_ERR_UNSUPPORTED";
+        case FSA_ERR_WORKSPACE: return "FSA_ERR_WORKSPACE";
+        case FSA_ERR_HIP: return "FSA_ERR_HIP";
+        case FSA_ERR_NOMEM: return "FSA_ERR_NOMEM";
+    }
+    return "FSA_ERR_UNKNOWN";
+}
+
+extern "C" const char* fsa_last_error(void) { return fsa::g_last_error; }
+
+extern "C" fsa_status fsa_bounds(const fsa_plan* plan, const void* Q, const void* K, void* ws,
+                                 float scale, hipStream_t stream) {
+    if (!plan || !Q || !K) {
+        set_error("fsa_bounds: NULL plan, Q or K");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!good_scale(scale)) {
+        set_error("fsa_bounds: scale must be finite and > 0 (got %g)", double(scale));
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(Q, 16) || !aligned(K, 16)) {
+        set_error("fsa_bounds: Q and K must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!ws || !aligned(ws, 256)) {
+        set_error("fsa_bounds: workspace missing or not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    return fsa::launch_bounds(*plan, Q, K, ws, scale, stream);
+}
+
+extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const void* K,
+                                  const void* V, void* O, const void* ws, float scale,
+                                  int32_t mode, hipStream_t stream) {
+    if (!plan || !Q || !K || !V || !O) {
+        set_error("fsa_forward: NULL plan, Q, K, V or O");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!good_scale(scale)) {
+        set_error("fsa_forward: scale must be finite and > 0 (got %g)", double(scale));
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY) {
+        set_error("fsa_forward: unknown mode %d", mode);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) {
+        set_error("fsa_forward: Q, K, V and O must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!ws || !aligned(ws, 256)) {
+        set_error("fsa_forward: workspace missing or not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    const size_t nb = tensor_bytes(*plan);
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
+        overlaps(O, nb, ws, plan->ws.total)) {
+        set_error("fsa_forward: O overlaps Q, K, V or the workspace");
+        return FSA_ERR_INVALID_ARG;
+    }
+    return fsa::launch_forward(*plan, Q, K, V, O, ws, scale, mode, stream);
+}
+
+namespace {
+
+using Key = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t>;
+
+std::mutex g_cache_mu;
+std::map<Key, fsa_plan*> g_cache;
+
+// Looks up or builds the plan of a shape (bq = bk = 0). Caller holds no lock.
+fsa_status cached_plan(const fsa_shape& s, const fsa_plan** out) {
+    const Key key{s.B, s.H, s.F, s.T, s.d, s.window, s.ref_frame, s.dtype};
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    auto it = g_cache.find(key);
+    if (it != g_cache.end()) {
+        *out = it->second;
+        return FSA_OK;
+    }
+    fsa_plan* p = nullptr;
+    fsa_status st = fsa_plan_create(&s, &p);
+    if (st != FSA_OK) return st;
+    try {
+        g_cache.emplace(key, p);
+    } catch (...) {
+        fsa_plan_destroy(p);
+        set_error("fsa_attention: out of host memory");
+        return FSA_ERR_NOMEM;
+    }
+    *out = p;
+    return FSA_OK;
+}
+
+fsa_shape make_shape(int32_t F, int32_t T, int32_t window, int32_t ref_frame, int32_t B,
+                     int32_t H, int32_t d, int32_t dtype) {
+    fsa_shape s;
+    s.B = B; s.H = H; s.F = F; s.T = T; s.d = d;
+    s.window = window; s.ref_frame = ref_frame; s.bq = 0; s.bk = 0; s.dtype = dtype;
+    return s;
+}
+
+}  // namespace
+
+extern "C" void fsa_cache_clear(void) {
+    std::lock_guard<std::mutex> lock(g_cache_mu);
+    for (auto& kv : g_cache) fsa_plan_destroy(kv.second);
+    g_cache.clear();
+}
+
+extern "C" size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t window,
+                                                int32_t ref_frame, int32_t B, int32_t H,
+                                                int32_t d, int32_t dtype) {
+    const fsa_plan* p = nullptr;
+    if (cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), &p) != FSA_OK) return 0;
+    return p->ws.total;
+}
+
+extern "C" fsa_status fsa_attention(const void* Q, const void* K, const void* V, void* O,
+                                    int32_t F, int32_t T, int32_t window, int32_t ref_frame,
+                                    float scale, int32_t B, int32_t H, int32_t d, int32_t dtype,
+                                    int32_t mode, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    if (!Q || !K || !V || !O) {
+        set_error("fsa_attention: NULL Q, K, V or O");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!good_scale(scale)) {
+        set_error("fsa_attention: scale must be finite and > 0 (got %g)", double(scale));
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY) {
+        set_error("fsa_attention: unknown mode %d", mode);
+        return FSA_ERR_INVALID_ARG;
+    }
+    const fsa_plan* p = nullptr;
+    fsa_status st = cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), &p);
+    if (st != FSA_OK) return st;
+    if (!ws || ws_bytes < p->ws.total) {
+        set_error("fsa_attention: workspace of %zu bytes, %zu needed", ws ? ws_bytes : size_t(0),
+                  p->ws.total);
+        return FSA_ERR_WORKSPACE;
+    }
+    const size_t nb = tensor_bytes(*p);
+    if (overlaps(O, nb, K, nb)) {
+        set_error("fsa_attention: O overlaps K");
+        return FSA_ERR_INVALID_ARG;
+    }
+    // Validate both calls before launching either.
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) {
+        set_error("fsa_attention: Q, K, V and O must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(ws, 256)) {
+        set_error("fsa_attention: workspace not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, V, nb) || overlaps(O, nb, ws, p->ws.total)) {
+        set_error("fsa_attention: O overlaps Q, V or the workspace");
+        return FSA_ERR_INVALID_ARG;
+    }
+    st = fsa_bounds(p, Q, K, ws, scale, stream);
+    if (st != FSA_OK) return st;
+    return fsa_forward(p, Q, K, V, O, ws, scale, mode, stream);
+}

@@ -1,0 +1,250 @@
+// Bounds kernels: key mean, centred keys, norms and per-head eligibility.
+//
+// Source: "HeyGen 与 Google Cloud：将 Avatar IV 部署到 TPU"
+// (news.xcc.im/article/5328), "Unchaining the Softmax" ¶2-¶3. By
+// Cauchy-Schwarz a row's largest logit is at most its query norm times the
+// largest key norm; centring the keys on their mean first leaves the softmax
+// unchanged and tightens that bound; with windowed slices the key maximum is
+// taken over the row's own slice; heads whose bound is too loose are flagged
+// for the online route.
+//
+// HBM-bound: K is read twice (mean, then centring), Q once, Kc written once.
+// Every reduction is deterministic: sums in a fixed order, maxima exact.
+#include <hip/hip_runtime.h>
+
+#include "fsa_internal.h"
+
+namespace {
+
+using fsa::FrameTable;
+
+template <typename E>
+struct Pack16 {                      // one 16-byte vector of E
+    static constexpr int n = 16 / sizeof(E);
+    E v[n];
+};
+
+template <typename E>
+__device__ __forceinline__ Pack16<E> load16(const E* p) {
+    Pack16<E> r;
+    *reinterpret_cast<uint4*>(r.v) = *reinterpret_cast<const uint4*>(p);
+    return r;
+}
+
+template <typename E>
+__device__ __forceinline__ void store16(E* p, const Pack16<E>& r) {
+    *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(r.v);
+}
+
+// Rows of one workgroup: part `part` of the frame grid, never crossing a frame.
+struct PartRows {
+    int begin, end;
+};
+
+__device__ __forceinline__ PartRows part_rows(int part, int T, int rows_per_part, int ppf) {
+    const int frame = part / ppf, sub = part % ppf;
+    PartRows r;
+    r.begin = frame * T + sub * rows_per_part;
+    r.end = min(frame * T + T, r.begin + rows_per_part);
+    return r;
+}
+
+// Pass 1: per-part column sums of K (for the mean) and row norms of Q.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bounds_colsum_qnorm(
+    const E* __restrict__ Q, const E* __restrict__ K, float* __restrict__ colsum,
+    float* __restrict__ qnorm, int N, int T, int rows_per_part, int ppf, int nparts) {
+    constexpr int V = Pack16<E>::n;
+    constexpr int LPR = D / V;        // lanes per row
+    constexpr int RPI = 256 / LPR;    // rows per iteration
+    __shared__ float red[RPI][D];
+
+    const int part = blockIdx.x, bh = blockIdx.y;
+    const PartRows pr = part_rows(part, T, rows_per_part, ppf);
+    const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+    const size_t base = size_t(bh) * N * D;
+
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = 0.f;
+    for (int r = pr.begin + r0; r < pr.end; r += RPI) {
+        const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
+        const Pack16<E> q = load16(Q + base + size_t(r) * D + lane * V);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            acc[e] += float(k.v[e]);
+            const float qe = float(q.v[e]);
+            ss = fmaf(qe, qe, ss);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) qnorm[size_t(bh) * N + r] = sqrtf(ss);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) red[r0][lane * V + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float s = 0.f;
+        for (int i = 0; i < RPI; ++i) s += red[i][threadIdx.x];
+        colsum[(size_t(bh) * nparts + part) * D + threadIdx.x] = s;
+    }
+}
+
+// Pass 2: the key mean of each (batch, head), summing the parts in order.
+template <int D>
+__global__ __launch_bounds__(256) void bounds_mean(const float* __restrict__ colsum,
+                                                   float* __restrict__ mu, int N, int nparts) {
+    const int bh = blockIdx.x, t = threadIdx.x;
+    if (t >= D) return;
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += colsum[(size_t(bh) * nparts + p) * D + t];
+    mu[size_t(bh) * D + t] = s / float(N);
+}
+
+// Pass 3: Kc = round(K - mu) to E, and the part's largest ||Kc_j|| computed
+// from the rounded values the forward kernel will consume.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bounds_centre(
+    const E* __restrict__ K, const float* __restrict__ mu, E* __restrict__ Kc,
+    float* __restrict__ partmax, int N, int T, int rows_per_part, int ppf, int nparts) {
+    constexpr int V = Pack16<E>::n;
+    constexpr int LPR = D / V;
+    constexpr int RPI = 256 / LPR;
+    __shared__ float red[RPI];
+
+    const int part = blockIdx.x, bh = blockIdx.y;
+    const PartRows pr = part_rows(part, T, rows_per_part, ppf);
+    const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+    const size_t base = size_t(bh) * N * D;
+
+    float m[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) m[e] = mu[size_t(bh) * D + lane * V + e];
+    float best = 0.f;
+    for (int r = pr.begin + r0; r < pr.end; r += RPI) {
+        const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
+        Pack16<E> c;
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            c.v[e] = E(float(k.v[e]) - m[e]);
+            const float ce = float(c.v[e]);
+            ss = fmaf(ce, ce, ss);
+        }
+        store16(Kc + base + size_t(r) * D + lane * V, c);
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        best = fmaxf(best, sqrtf(ss));
+    }
+    if (lane == 0) red[r0] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = 0.f;
+        for (int i = 0; i < RPI; ++i) b = fmaxf(b, red[i]);
+        partmax[size_t(bh) * nparts + part] = b;
+    }
+}
+
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+    for (int w = 1; w < int(blockDim.x >> 6); ++w) r = fmaxf(r, scratch[w]);
+    return r;
+}
+
+// Pass 4, per (batch, head): per-frame key radius, per-slice radius, the
+// largest row bound scale * ||q_i|| * R_S(f(i)) and the eligibility flag.
+__global__ __launch_bounds__(256) void bounds_finalize(
+    const float* __restrict__ qnorm, const float* __restrict__ partmax, float* __restrict__ rframe,
+    float* __restrict__ rslice, float* __restrict__ stat, uint8_t* __restrict__ elig, int N,
+    int T, int F, int ppf, float scale, const FrameTable tab) {
+    __shared__ float rf[FSA_MAX_FRAMES + 1];
+    __shared__ float qm[FSA_MAX_FRAMES + 1];
+    __shared__ float scratch[4];
+    const int bh = blockIdx.x;
+    for (int g = threadIdx.x; g < F; g += blockDim.x) {
+        float b = 0.f;
+        for (int s = 0; s < ppf; ++s) b = fmaxf(b, partmax[size_t(bh) * F * ppf + g * ppf + s]);
+        rf[g] = b;
+        rframe[size_t(bh) * F + g] = b;
+    }
+    for (int f = 0; f < F; ++f) {
+        float b = 0.f;
+        for (int i = threadIdx.x; i < T; i += blockDim.x)
+            b = fmaxf(b, qnorm[size_t(bh) * N + size_t(f) * T + i]);
+        b = block_max(b, scratch);
+        if (threadIdx.x == 0) qm[f] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float st = 0.f;
+        for (int f = 0; f < F; ++f) {
+            const uint32_t run = tab.runs[f];
+            const int a0 = run & 0xff, l0 = (run >> 8) & 0xff;
+            const int a1 = (run >> 16) & 0xff, l1 = run >> 24;
+            float r = 0.f;
+            for (int g = a0; g < a0 + l0; ++g) r = fmaxf(r, rf[g]);
+            for (int g = a1; g < a1 + l1; ++g) r = fmaxf(r, rf[g]);
+            rslice[size_t(bh) * F + f] = r;
+            st = fmaxf(st, (scale * qm[f]) * r);
+        }
+        stat[bh] = st;
+        elig[bh] = st <= FSA_ELIG_BETA ? 1 : 0;
+    }
+}
+
+template <typename E, int D>
+fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* wsv, float scale,
+                      hipStream_t stream) {
+    const fsa_shape& s = p.shape;
+    const int N = s.F * s.T, BH = s.B * s.H;
+    const int ppf = p.bounds.parts_per_frame, nparts = s.F * ppf;
+    char* ws = static_cast<char*>(wsv);
+    const E* Q = static_cast<const E*>(Qv);
+    const E* K = static_cast<const E*>(Kv);
+    E* Kc = reinterpret_cast<E*>(ws + p.ws.kc);
+    float* mu = reinterpret_cast<float*>(ws + p.ws.mu);
+    float* qn = reinterpret_cast<float*>(ws + p.ws.qnorm);
+    float* colsum = reinterpret_cast<float*>(ws + p.bounds.colsum);
+    float* partmax = reinterpret_cast<float*>(ws + p.bounds.partmax);
+    const dim3 grid(nparts, BH);
+    hipLaunchKernelGGL((bounds_colsum_qnorm<E, D>), grid, dim3(256), 0, stream, Q, K, colsum, qn,
+                       N, s.T, p.bounds.rows_per_part, ppf, nparts);
+    hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, N, nparts);
+    hipLaunchKernelGGL((bounds_centre<E, D>), grid, dim3(256), 0, stream, K, mu, Kc, partmax, N,
+                       s.T, p.bounds.rows_per_part, ppf, nparts);
+    hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, qn, partmax,
+                       reinterpret_cast<float*>(ws + p.ws.rframe),
+                       reinterpret_cast<float*>(ws + p.ws.rslice),
+                       reinterpret_cast<float*>(ws + p.ws.stat),
+                       reinterpret_cast<uint8_t*>(ws + p.ws.elig), N, s.T, s.F, ppf, scale,
+                       p.table);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return FSA_OK;
+}
+
+}  // namespace
+
+namespace fsa {
+
+fsa_status launch_bounds(const fsa_plan& p, const void* Q, const void* K, void* ws, float scale,
+                         hipStream_t stream) {
+    const bool bf16 = p.shape.dtype == FSA_BF16;
+    if (p.shape.d == 128)
+        return bf16 ? run_bounds<__bf16, 128>(p, Q, K, ws, scale, stream)
+                    : run_bounds<float, 128>(p, Q, K, ws, scale, stream);
+    return bf16 ? run_bounds<__bf16, 64>(p, Q, K, ws, scale, stream)
+                : run_bounds<float, 64>(p, Q, K, ws, scale, stream);
+}
+
+}  // namespace fsa

@@ -1,0 +1,311 @@
+"""ctypes binding of libfsa (include/fsa.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and passes
+plain pointers and sizes through; all computation happens in the library's
+HIP kernels (or, for the plan, its host C++). Tensors are torch tensors on
+the GPU, used only as device memory; the stream is torch's current HIP
+stream unless one is given.
+
+There is no fallback: if libfsa.so is missing the import of the library
+raises, and every call that fails in the library raises FsaError with the
+library's own error text.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsa.so")
+
+FSA_OK = 0
+FSA_ERR_INVALID_ARG = -1
+FSA_ERR_UNSUPPORTED = -2
+FSA_ERR_WORKSPACE = -3
+FSA_ERR_HIP = -4
+FSA_ERR_NOMEM = -5
+
+FSA_BF16 = 0
+FSA_F32 = 1
+
+FSA_MODE_AUTO = 0
+FSA_MODE_ONLINE_ONLY = 1
+FSA_MODE_FIXED_ONLY = 2
+MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MODE_FIXED_ONLY}
+
+FSA_ELIG_BETA = 32.0
+FSA_MAX_FRAMES = 255
+
+# Every symbol include/fsa.h declares.
+EXPORTS = (
+    "fsa_plan_create", "fsa_plan_destroy", "fsa_plan_shape", "fsa_plan_export",
+    "fsa_plan_valid_pairs", "fsa_workspace_bytes", "fsa_workspace_layout",
+    "fsa_bounds", "fsa_forward", "fsa_attention", "fsa_attention_workspace_bytes",
+    "fsa_cache_clear", "fsa_status_string", "fsa_last_error",
+)
+
+
+class fsa_shape(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("B", "H", "F", "T", "d", "window", "ref_frame",
+                                        "bq", "bk", "dtype")]
+
+
+class fsa_ws_layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("kc", "mu", "qnorm", "rframe", "rslice", "stat",
+                                         "elig", "total")]
+
+
+class FsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfsa.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    L.fsa_plan_create.argtypes = [POINTER(fsa_shape), POINTER(P)]
+    L.fsa_plan_create.restype = c_int32
+    L.fsa_plan_destroy.argtypes = [P]
+    L.fsa_plan_destroy.restype = None
+    L.fsa_plan_shape.argtypes = [P, POINTER(fsa_shape)]
+    L.fsa_plan_shape.restype = c_int32
+    L.fsa_plan_export.argtypes = [P, P, P, P, P, POINTER(c_int32), POINTER(c_int64)]
+    L.fsa_plan_export.restype = c_int32
+    L.fsa_plan_valid_pairs.argtypes = [P]
+    L.fsa_plan_valid_pairs.restype = c_int64
+    L.fsa_workspace_bytes.argtypes = [P]
+    L.fsa_workspace_bytes.restype = c_size_t
+    L.fsa_workspace_layout.argtypes = [P, POINTER(fsa_ws_layout)]
+    L.fsa_workspace_layout.restype = c_int32
+    L.fsa_bounds.argtypes = [P, P, P, P, c_float, P]
+    L.fsa_bounds.restype = c_int32
+    L.fsa_forward.argtypes = [P, P, P, P, P, P, c_float, c_int32, P]
+    L.fsa_forward.restype = c_int32
+    L.fsa_attention.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_float,
+                                c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]
+    L.fsa_attention.restype = c_int32
+    L.fsa_attention_workspace_bytes.argtypes = [c_int32] * 8
+    L.fsa_attention_workspace_bytes.restype = c_size_t
+    L.fsa_cache_clear.argtypes = []
+    L.fsa_cache_clear.restype = None
+    L.fsa_status_string.argtypes = [c_int32]
+    L.fsa_status_string.restype = c_char_p
+    L.fsa_last_error.argtypes = []
+    L.fsa_last_error.restype = c_char_p
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().fsa_status_string(status).decode()
+    except Exception:   # noqa: BLE001 - naming only
+        return str(status)
+
+
+def _check(status: int) -> None:
+    if status != FSA_OK:
+        raise FsaError(status, fsa_last_error())
+
+
+def fsa_status_string(status: int) -> str:
+    return lib().fsa_status_string(status).decode()
+
+
+def fsa_last_error() -> str:
+    return lib().fsa_last_error().decode()
+
+
+def _ptr(t) -> int | None:
+    """Device (or host) address of a tensor, an int, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ plan
+
+class Plan:
+    """Owns an fsa_plan handle (host memory)."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.fsa_plan_destroy(self.handle)
+            self.handle = None
+
+    @property
+    def _as_parameter_(self):
+        return c_void_p(self.handle)
+
+
+def make_shape(B, H, F, T, d, window, ref_frame, bq=0, bk=0, dtype=FSA_BF16) -> fsa_shape:
+    return fsa_shape(B, H, F, T, d, window, ref_frame, bq, bk, dtype)
+
+
+def fsa_plan_create(shape: fsa_shape) -> Plan:
+    h = c_void_p()
+    _check(lib().fsa_plan_create(ctypes.byref(shape), ctypes.byref(h)))
+    return Plan(h.value)
+
+
+def fsa_plan_destroy(plan: Plan) -> None:
+    if plan.handle:
+        lib().fsa_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def fsa_plan_shape(plan: Plan) -> fsa_shape:
+    s = fsa_shape()
+    _check(lib().fsa_plan_shape(plan, ctypes.byref(s)))
+    return s
+
+
+def fsa_plan_export(plan: Plan) -> dict:
+    """The tile list as numpy int32 arrays (row_ptr, col_idx, qframe, runs)."""
+    L = lib()
+    nq = c_int32()
+    nnz = c_int64()
+    _check(L.fsa_plan_export(plan, None, None, None, None, ctypes.byref(nq), ctypes.byref(nnz)))
+    row_ptr = np.zeros(nq.value + 1, np.int32)
+    col_idx = np.zeros(nnz.value, np.int32)
+    qframe = np.zeros(nq.value, np.int32)
+    runs = np.zeros((nq.value, 4), np.int32)
+    _check(L.fsa_plan_export(plan, row_ptr.ctypes.data, col_idx.ctypes.data,
+                             qframe.ctypes.data, runs.ctypes.data, None, None))
+    return {"row_ptr": row_ptr, "col_idx": col_idx, "qframe": qframe, "runs": runs,
+            "n_qblocks": nq.value, "nnz": nnz.value}
+
+
+def fsa_plan_valid_pairs(plan: Plan) -> int:
+    return int(lib().fsa_plan_valid_pairs(plan))
+
+
+def fsa_workspace_bytes(plan: Plan) -> int:
+    return int(lib().fsa_workspace_bytes(plan))
+
+
+def fsa_workspace_layout(plan: Plan) -> dict:
+    w = fsa_ws_layout()
+    _check(lib().fsa_workspace_layout(plan, ctypes.byref(w)))
+    return {n: int(getattr(w, n)) for n, _ in fsa_ws_layout._fields_}
+
+
+# ------------------------------------------------------------------ launches
+
+def fsa_bounds(plan: Plan, Q, K, ws, scale: float, stream=None) -> None:
+    _check(lib().fsa_bounds(plan, _ptr(Q), _ptr(K), _ptr(ws), float(scale), _stream(stream)))
+
+
+def fsa_forward(plan: Plan, Q, K, V, O, ws, scale: float, mode=FSA_MODE_AUTO,
+                stream=None) -> None:
+    mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().fsa_forward(plan, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(ws), float(scale),
+                             mode, _stream(stream)))
+
+
+def fsa_attention(Q, K, V, O, F, T, window, ref_frame, scale, B, H, d, dtype, mode, ws,
+                  ws_bytes, stream=None) -> None:
+    mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().fsa_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), F, T, window, ref_frame,
+                               float(scale), B, H, d, dtype, mode, _ptr(ws), int(ws_bytes),
+                               _stream(stream)))
+
+
+def fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, dtype) -> int:
+    n = int(lib().fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, dtype))
+    if n == 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, fsa_last_error())
+    return n
+
+
+def fsa_cache_clear() -> None:
+    lib().fsa_cache_clear()
+
+
+# ------------------------------------------------------------------ torch helpers
+
+def dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FSA_BF16
+    if t.dtype == torch.float32:
+        return FSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def attention(q, k, v, F: int, T: int, window: int, ref_frame: int, scale: float | None = None,
+              mode="auto", out=None, ws=None):
+    """O = frame-aligned windowed attention of [B, H, F*T, d] CUDA tensors.
+
+    Calls fsa_attention on torch's current stream; allocates O and the
+    workspace with torch unless given.
+    """
+    import torch
+    B, H, N, d = q.shape
+    if N != F * T:
+        raise ValueError(f"N={N} != F*T={F * T}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one shape and dtype")
+    if scale is None:
+        scale = d ** -0.5
+    code = dtype_code(q)
+    need = fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, code)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    fsa_attention(q, k, v, out, F, T, window, ref_frame, scale, B, H, d, code, mode, ws,
+                  ws.numel() * ws.element_size())
+    return out
+
+
+def workspace_views(plan: Plan, ws):
+    """Typed torch views of the bound products inside a workspace tensor."""
+    import torch
+    s = fsa_plan_shape(plan)
+    lay = fsa_workspace_layout(plan)
+    BH, N = s.B * s.H, s.F * s.T
+    kdt = torch.bfloat16 if s.dtype == FSA_BF16 else torch.float32
+    esz = 2 if s.dtype == FSA_BF16 else 4
+
+    def view(off, n, dt, sz, shape):
+        return ws[off:off + n * sz].view(dt).view(*shape)
+
+    return {
+        "kc": view(lay["kc"], BH * N * s.d, kdt, esz, (s.B, s.H, N, s.d)),
+        "mu": view(lay["mu"], BH * s.d, torch.float32, 4, (s.B, s.H, s.d)),
+        "qnorm": view(lay["qnorm"], BH * N, torch.float32, 4, (s.B, s.H, N)),
+        "rframe": view(lay["rframe"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
+        "rslice": view(lay["rslice"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
+        "stat": view(lay["stat"], BH, torch.float32, 4, (s.B, s.H)),
+        "elig": view(lay["elig"], BH, torch.uint8, 1, (s.B, s.H)),
+    }

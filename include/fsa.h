@@ -1,0 +1,203 @@
+/*
+ * fsa.h -- C ABI of libfsa: frame-aligned windowed sparse attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the page "HeyGen 与 Google Cloud：将 Avatar IV 部署到
+ * TPU" (news.xcc.im/article/5328), English text. Citations name its section
+ * and paragraph (figure captions are not counted as paragraphs).
+ *
+ * The operation. A chunk of F video frames of T tokens each (N = F*T tokens,
+ * frame-major: token n lies in frame n / T) is attended head by head. Queries
+ * of frame f see the keys of the frames in
+ *     S(f) = { g : 0 <= g < F, |g - f| <= window }  U  { ref_frame }
+ * and nothing else ("Deleting the Mask" ¶1), with scores scale * <q_i, k_j>
+ * and a softmax over that slice:
+ *     O_i = sum_j softmax_j(scale * q_i . k_j) v_j ,  j in frames S(f(i)).
+ * The window is clipped at the chunk edges; the reference frame is joined as
+ * a set union; the reference frame's own queries see only their own slice;
+ * there is no causal masking inside a frame.
+ *
+ * Route (changes rounding only, never the exact result):
+ *  - tiling in blocks that are multiples of 16 tokens and divide T, so each
+ *    (query block, key block) tile is entirely inside or outside the mask and
+ *    the reference frame is just more full blocks in one pass
+ *    ("Deleting the Mask" ¶2);
+ *  - keys centred by their mean over the chunk, and a per-row softmax shift
+ *    fixed in advance at the Cauchy-Schwarz bound
+ *    scale * ||q_i|| * max_{j in slice} ||k_j - mu||, which removes the
+ *    running-max rescale ("Unchaining the Softmax" ¶2, ¶3);
+ *  - heads whose bound is loose (largest row bound > FSA_ELIG_BETA) use the
+ *    online softmax inside the same kernel ("Unchaining the Softmax" ¶3);
+ *  - bf16 inputs: the P.V product takes P rounded to bf16, fp32 accumulation
+ *    ("Proving the Pixels Didn't Change" ¶2).
+ *
+ * Layout. Q, K, V, O are [B][H][N][d] contiguous, d fastest, in the dtype
+ * given by the shape; base pointers 16-byte aligned; device memory.
+ *
+ * Ownership. The caller owns Q, K, V, O and the workspace (device memory of
+ * fsa_workspace_bytes() bytes, 256-byte aligned). The library never frees
+ * them, never writes K, and never allocates device memory in fsa_bounds,
+ * fsa_forward or fsa_attention. A plan is host memory only.
+ *
+ * Errors. Every call validates its arguments synchronously before any
+ * launch and returns a status; nothing is launched on an error. Kernel faults
+ * surface at the caller's next synchronisation. fsa_last_error() gives the
+ * calling thread's last error detail. No C++ exception crosses the ABI.
+ *
+ * Streams. Work is enqueued on the given HIP stream (0 = the null stream)
+ * and is asynchronous to the host unless stated.
+ */
+#ifndef FSA_H
+#define FSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FSA_OK = 0,
+    FSA_ERR_INVALID_ARG = -1,   /* a value outside its documented range */
+    FSA_ERR_UNSUPPORTED = -2,   /* a valid request this build cannot do   */
+    FSA_ERR_WORKSPACE = -3,     /* workspace missing, too small, unaligned */
+    FSA_ERR_HIP = -4,           /* a HIP runtime call failed              */
+    FSA_ERR_NOMEM = -5          /* host allocation failed                 */
+} fsa_status;
+
+typedef enum { FSA_BF16 = 0, FSA_F32 = 1 } fsa_dtype;
+
+typedef enum {
+    FSA_MODE_AUTO = 0,          /* per head: fixed max if eligible, else online */
+    FSA_MODE_ONLINE_ONLY = 1,   /* every head online (the A/B baseline)         */
+    FSA_MODE_FIXED_ONLY = 2     /* every head fixed max (tests: shows why the
+                                   fallback exists; loose heads underflow)      */
+} fsa_mode;
+
+/* Eligibility threshold on a head's largest row bound, in logit units. */
+#define FSA_ELIG_BETA 32.0f
+/* Largest frame count a plan accepts. */
+#define FSA_MAX_FRAMES 255
+
+typedef struct {
+    int32_t B, H;        /* batch, heads (>= 1)                                */
+    int32_t F, T;        /* frames (1..FSA_MAX_FRAMES), tokens per frame
+                            (multiple of 16)                                   */
+    int32_t d;           /* head width: 64 or 128                              */
+    int32_t window;      /* frames on each side of the query frame (>= 0)      */
+    int32_t ref_frame;   /* reference frame, 0 <= ref_frame < F                */
+    int32_t bq, bk;      /* tile-list block sizes: multiples of 16 dividing T;
+                            0 = choose                                         */
+    int32_t dtype;       /* fsa_dtype of Q, K, V, O                            */
+} fsa_shape;
+
+typedef struct fsa_plan fsa_plan;   /* opaque, host memory only */
+
+/* Byte offsets of the bound products inside a workspace. */
+typedef struct {
+    size_t kc;      /* centred keys, [B][H][N][d], the input dtype             */
+    size_t mu;      /* key mean, float [B][H][d]                               */
+    size_t qnorm;   /* ||q_i||, float [B][H][N]                                */
+    size_t rframe;  /* max_{j in frame g} ||k_j - mu||, float [B][H][F]        */
+    size_t rslice;  /* max over the frames of S(f) of rframe, float [B][H][F]  */
+    size_t stat;    /* scale * max_i ||q_i|| rslice(f(i)), float [B][H]        */
+    size_t elig;    /* 1 if stat <= FSA_ELIG_BETA else 0, uint8 [B][H]         */
+    size_t total;   /* bytes needed (== fsa_workspace_bytes)                   */
+} fsa_ws_layout;
+
+/*
+ * fsa_plan_create -- build the frame-aligned tile list for a shape
+ * ("Deleting the Mask" ¶2): q-blocks of bq tokens and k-blocks of bk tokens,
+ * both multiples of 16 that divide T, so no block straddles a frame. Tile
+ * (qb, kb) is live iff the frame of kb is in S(frame of qb); a live tile is
+ * full by construction. Rows in ascending qb, columns in ascending kb.
+ * Host work only (no HIP call); *out is owned by the caller and freed with
+ * fsa_plan_destroy. Errors: FSA_ERR_INVALID_ARG (NULL pointers, B, H, F or
+ * T < 1, window < 0, ref_frame outside [0,F), bq or bk neither 0 nor a
+ * multiple of 16 dividing T, dtype not an fsa_dtype), FSA_ERR_UNSUPPORTED
+ * (T % 16 != 0, d not 64 or 128, F above FSA_MAX_FRAMES, B*H*N*d above
+ * 2^31 - 1 elements per tensor), FSA_ERR_NOMEM.
+ */
+fsa_status fsa_plan_create(const fsa_shape* shape, fsa_plan** out);
+void fsa_plan_destroy(fsa_plan* plan);
+
+/* The shape a plan was built for, with bq and bk resolved. */
+fsa_status fsa_plan_shape(const fsa_plan* plan, fsa_shape* out);
+
+/*
+ * fsa_plan_export -- copy the tile list out in CSR form (host arrays).
+ * row_ptr: int32[n_qblocks + 1]; col_idx: int32[nnz]; qframe: int32[n_qblocks]
+ * (frame of each q-block); runs: int32[n_qblocks * 4], per q-block up to two
+ * maximal ranges of consecutive live k-blocks as key-token ranges
+ * {start0, end0, start1, end1} (unused range = {0, 0}). Any array pointer may
+ * be NULL (skipped); n_qblocks and nnz (may be NULL) receive the sizes, so a
+ * call with all arrays NULL is a size query.
+ */
+fsa_status fsa_plan_export(const fsa_plan* plan, int32_t* row_ptr, int32_t* col_idx,
+                           int32_t* qframe, int32_t* runs,
+                           int32_t* n_qblocks, int64_t* nnz);
+
+/* Valid (query, key) pairs of one (batch, head): T^2 * sum_f |S(f)|. */
+int64_t fsa_plan_valid_pairs(const fsa_plan* plan);
+
+/* Workspace size in bytes for this plan, and where each product lives. */
+size_t fsa_workspace_bytes(const fsa_plan* plan);
+fsa_status fsa_workspace_layout(const fsa_plan* plan, fsa_ws_layout* out);
+
+/*
+ * fsa_bounds -- per (batch, head): key mean mu over all N keys (fp32, fixed
+ * reduction order), centred keys Kc = round(K - mu) to the input dtype,
+ * per-frame max ||Kc_j|| computed from the rounded Kc, per-slice max, row
+ * norms ||q_i||, the head statistic and its eligibility flag
+ * ("Unchaining the Softmax" ¶2, ¶3). Q and K are read; results go to ws.
+ * scale > 0 and finite. Deterministic: no atomics, fixed reduction trees.
+ * Errors: FSA_ERR_INVALID_ARG (NULL plan/pointers, bad scale),
+ * FSA_ERR_WORKSPACE (ws NULL or not 256-byte aligned), FSA_ERR_HIP.
+ */
+fsa_status fsa_bounds(const fsa_plan* plan, const void* Q, const void* K, void* ws,
+                      float scale, hipStream_t stream);
+
+/*
+ * fsa_forward -- the attention itself, one launch. Reads Q, K, V and the
+ * bound products in ws (Kc, qnorm, rslice, elig) written by fsa_bounds for the
+ * same plan, inputs and scale; writes O. Per (batch, head), mode picks the
+ * route: AUTO takes the fixed max where elig = 1 and the online softmax
+ * elsewhere. The fixed-max route scores the centred keys Kc (its bound holds
+ * for them); the online route is the standard one and scores the keys K as
+ * given, so a loose head's large keys are never re-rounded by centring
+ * ("Unchaining the Softmax" ¶3). O must not overlap Q, K, V or ws.
+ * Errors: FSA_ERR_INVALID_ARG (NULL pointers, bad scale or mode, misaligned
+ * tensors, O overlapping an input), FSA_ERR_WORKSPACE, FSA_ERR_HIP.
+ */
+fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const void* K, const void* V,
+                       void* O, const void* ws, float scale, int32_t mode, hipStream_t stream);
+
+/*
+ * fsa_attention -- fsa_bounds then fsa_forward with a plan built for the
+ * given shape and cached per shape (bq = bk = 0, the cache is guarded by a
+ * mutex; this is the only call that allocates, host memory, on a cache miss).
+ * ws must hold at least fsa_workspace_bytes() of that plan (ws_bytes says how
+ * much it holds). Errors as fsa_plan_create, fsa_bounds and fsa_forward.
+ */
+fsa_status fsa_attention(const void* Q, const void* K, const void* V, void* O,
+                         int32_t F, int32_t T, int32_t window, int32_t ref_frame,
+                         float scale, int32_t B, int32_t H, int32_t d, int32_t dtype,
+                         int32_t mode, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fsa_attention needs for this shape (0 on invalid input). */
+size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t window, int32_t ref_frame,
+                                     int32_t B, int32_t H, int32_t d, int32_t dtype);
+
+/* Drop every cached plan of fsa_attention. */
+void fsa_cache_clear(void);
+
+const char* fsa_status_string(fsa_status status);
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* fsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FSA_H */

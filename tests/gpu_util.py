@@ -1,0 +1,90 @@
+"""Shared helpers of the GPU tests: run the HIP path through the C ABI and
+compare it with the fp64 oracle on the same drawn inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import fsa_oracle as orc
+from frame_aligned_block_amd import fsa
+from frame_aligned_block_amd.inputs import CONFIGS, Config, make_inputs, to_f64
+
+# Tolerances against the fp64 oracle.
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+F32_MAX_ABS = 1e-5
+
+
+def say(*a):
+    """Name the case before each GPU step (flushed, so a dying box still shows it)."""
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dtype_code(cfg: Config) -> int:
+    return fsa.FSA_BF16 if cfg.dtype == "bf16" else fsa.FSA_F32
+
+
+class Run:
+    """One bounds + forward pass of a config through the C ABI."""
+
+    def __init__(self, cfg: Config, seed=0, inputs=None, bq=0, bk=0):
+        self.cfg = cfg
+        if inputs is None:
+            inputs = make_inputs(cfg, seed=seed, device="cuda")
+        self.Q, self.K, self.V = inputs
+        shape = fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window, cfg.ref_frame,
+                               bq, bk, dtype_code(cfg))
+        self.plan = fsa.fsa_plan_create(shape)
+        self.ws = torch.zeros(fsa.fsa_workspace_bytes(self.plan), dtype=torch.uint8,
+                              device="cuda")
+        self.K_before = None
+
+    def bounds(self):
+        fsa.fsa_bounds(self.plan, self.Q, self.K, self.ws, self.cfg.scale)
+        return self
+
+    def forward(self, mode="auto"):
+        O = torch.full_like(self.Q, float("nan"))
+        fsa.fsa_forward(self.plan, self.Q, self.K, self.V, O, self.ws, self.cfg.scale, mode)
+        torch.cuda.synchronize()
+        return O
+
+    def views(self):
+        return fsa.workspace_views(self.plan, self.ws)
+
+
+def sample_rows(cfg: Config, n_random: int, seed: int) -> np.ndarray:
+    """First and last row of every frame plus random rows, sorted."""
+    rng = np.random.default_rng(seed)
+    edges = np.concatenate([[f * cfg.T, f * cfg.T + cfg.T - 1] for f in range(cfg.F)])
+    rows = np.concatenate([edges, rng.choice(cfg.N, n_random, replace=False)])
+    return np.unique(rows)
+
+
+def oracle_rows(cfg: Config, Q, K, V, b: int, h: int, rows, window=None, ref=None):
+    """Oracle output rows of head (b, h) for drawn tensors Q, K, V (any device)."""
+    q = to_f64(Q[b, h])[None, None]
+    k = to_f64(K[b, h])[None, None]
+    v = to_f64(V[b, h])[None, None]
+    w = cfg.window if window is None else window
+    r = cfg.ref_frame if ref is None else ref
+    return orc.attention_rows(q, k, v, cfg.F, cfg.T, w, r, cfg.scale, 0, 0, rows)
+
+
+def errors(got: torch.Tensor, want: np.ndarray):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    diff = np.abs(g - want)
+    return float(diff.max()), float(diff.mean()), bool(np.isfinite(g).all())
+
+
+def assert_close(cfg: Config, got: torch.Tensor, want: np.ndarray, what: str):
+    mx, mean, finite = errors(got, want)
+    assert finite, f"{what}: non-finite output"
+    if cfg.dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, f"{what}: max {mx:.3g} mean {mean:.3g}"
+    else:
+        assert mx <= F32_MAX_ABS, f"{what}: max {mx:.3g}"
+    return mx, mean

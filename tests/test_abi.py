@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: exported symbols and synchronous argument errors."""
+import os
+import re
+
+import pytest
+
+from frame_aligned_block_amd import fsa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    L = fsa.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(fsa.EXPORTS) == names
+
+
+def test_status_strings():
+    assert fsa.fsa_status_string(0) == "FSA_OK"
+    assert fsa.fsa_status_string(-3) == "FSA_ERR_WORKSPACE"
+
+
+def shape(**kw):
+    base = dict(B=1, H=2, F=5, T=48, d=64, window=1, ref_frame=0, bq=0, bk=0, dtype=fsa.FSA_F32)
+    base.update(kw)
+    return fsa.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=40), fsa.FSA_ERR_UNSUPPORTED),          # T % 16 != 0
+    (dict(d=96), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(F=256), fsa.FSA_ERR_UNSUPPORTED),
+    (dict(ref_frame=5), fsa.FSA_ERR_INVALID_ARG),
+    (dict(ref_frame=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(window=-1), fsa.FSA_ERR_INVALID_ARG),
+    (dict(B=0), fsa.FSA_ERR_INVALID_ARG),
+    (dict(bq=32), fsa.FSA_ERR_INVALID_ARG),         # does not divide 48
+    (dict(bk=24), fsa.FSA_ERR_INVALID_ARG),         # not a multiple of 16
+    (dict(dtype=7), fsa.FSA_ERR_INVALID_ARG),
+    (dict(H=40000, T=3600, F=13, d=128), fsa.FSA_ERR_UNSUPPORTED),   # > 2^31 elements
+])
+def test_plan_create_errors(kw, status):
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.fsa_plan_create(shape(**kw))
+    assert e.value.status == status
+    assert fsa.fsa_last_error()
+
+
+FAKE = 0x10000   # a 256-aligned address; never dereferenced: calls fail validation first
+
+
+def test_bounds_and_forward_validate_before_launch():
+    p = fsa.fsa_plan_create(shape())
+    cases = [
+        (lambda: fsa.fsa_bounds(p, None, FAKE, FAKE, 0.125, 0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds(p, FAKE, FAKE, FAKE, 0.0, 0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds(p, FAKE, FAKE, FAKE, float("nan"), 0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds(p, FAKE + 8, FAKE, FAKE, 0.125, 0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds(p, FAKE, FAKE, None, 0.125, 0), fsa.FSA_ERR_WORKSPACE),
+        (lambda: fsa.fsa_bounds(p, FAKE, FAKE, FAKE + 16, 0.125, 0), fsa.FSA_ERR_WORKSPACE),
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE, None, FAKE, 0.125, 0, 0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE, FAKE * 64, FAKE * 128, 0.125, 9, 0),
+         fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE, FAKE * 64, FAKE * 128, -1.0, 0, 0),
+         fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_forward(p, FAKE, None, FAKE, FAKE * 64, FAKE * 128, 0.125, 0, 0),
+         fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE, FAKE * 32, FAKE * 128, 0.125, 0, 0),
+         fsa.FSA_ERR_INVALID_ARG),     # O == K
+        # O aliasing Q / the workspace
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE * 64, FAKE + 256, FAKE * 128, 0.125, 0, 0),
+         fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE * 64, FAKE * 128, FAKE * 128, 0.125, 0, 0),
+         fsa.FSA_ERR_INVALID_ARG),
+    ]
+    for call, status in cases:
+        with pytest.raises(fsa.FsaError) as e:
+            call()
+        assert e.value.status == status, fsa.fsa_last_error()
+
+
+def test_attention_validates_before_launch():
+    F, T, w, r, B, H, d = 5, 48, 1, 0, 1, 2, 64
+    need = fsa.fsa_attention_workspace_bytes(F, T, w, r, B, H, d, fsa.FSA_F32)
+    assert need > B * H * F * T * d * 4
+    base = [FAKE, FAKE * 64, FAKE * 128, FAKE * 256, F, T, w, r, 0.125, B, H, d, fsa.FSA_F32,
+            0, FAKE * 512, need]
+    def call(**over):
+        args = list(base)
+        names = ["Q", "K", "V", "O", "F", "T", "window", "ref_frame", "scale", "B", "H", "d",
+                 "dtype", "mode", "ws", "ws_bytes"]
+        for k, v in over.items():
+            args[names.index(k)] = v
+        fsa.fsa_attention(*args, stream=0)
+    for over, status in [
+        (dict(ws_bytes=need - 1), fsa.FSA_ERR_WORKSPACE),
+        (dict(ws=None), fsa.FSA_ERR_WORKSPACE),
+        (dict(ws=FAKE * 512 + 64), fsa.FSA_ERR_WORKSPACE),
+        (dict(T=40), fsa.FSA_ERR_UNSUPPORTED),
+        (dict(d=32), fsa.FSA_ERR_UNSUPPORTED),
+        (dict(ref_frame=9), fsa.FSA_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), fsa.FSA_ERR_INVALID_ARG),
+        (dict(mode=3), fsa.FSA_ERR_INVALID_ARG),
+        (dict(O=FAKE * 64), fsa.FSA_ERR_INVALID_ARG),        # O == K
+        (dict(V=None), fsa.FSA_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(fsa.FsaError) as e:
+            call(**over)
+        assert e.value.status == status, (over, fsa.fsa_last_error())
+    fsa.fsa_cache_clear()

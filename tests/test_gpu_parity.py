@@ -1,0 +1,286 @@
+"""HIP path vs the fp64 oracle, through the C ABI (GPU).
+
+Bar: tile list and eligibility flags bit-exact; bf16 outputs within max-abs
+2e-2 and mean-abs 2e-3; fp32 outputs within max-abs 1e-5. Full outputs where
+the oracle is quick, sampled rows (every frame's first and last row plus
+random rows) at the full-size workloads, in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fsa_oracle as orc
+from frame_aligned_block_amd import fsa
+from frame_aligned_block_amd.inputs import CONFIGS, to_f64
+
+from gpu_util import (BF16_MAX_ABS, Run, assert_close, errors, oracle_rows, sample_rows,
+                      say)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU too; every test here is gpu-marked
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+# ------------------------------------------------------------------ bounds
+
+def check_bounds(run: Run, heads=None):
+    cfg = run.cfg
+    v = run.views()
+    heads = range(cfg.H) if heads is None else heads
+    for h in heads:
+        q = to_f64(run.Q[0, h])[None, None]
+        k = to_f64(run.K[0, h])[None, None]
+        want = orc.bounds(q, k, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        mu = v["mu"][0, h].double().cpu().numpy()
+        assert np.max(np.abs(mu - want["mu"][0, 0])) < 1e-4, h
+        qn = v["qnorm"][0, h].double().cpu().numpy()
+        assert np.allclose(qn, want["qnorm"][0, 0], rtol=2e-6, atol=1e-6), h
+        # norms of the bf16-rounded centred keys vs exact centring
+        rtol = 2e-3 if cfg.dtype == "bf16" else 1e-5
+        assert np.allclose(v["rframe"][0, h].double().cpu().numpy(), want["R"][0, 0], rtol=rtol), h
+        assert np.allclose(v["rslice"][0, h].double().cpu().numpy(), want["R_S"][0, 0], rtol=rtol), h
+        stat = float(v["stat"][0, h])
+        assert stat == pytest.approx(want["stat"][0, 0], rel=rtol), h
+        # flags bit-exact, and every head clear of the threshold by 5%
+        assert abs(want["stat"][0, 0] - orc.BETA) / orc.BETA > 0.05, (h, want["stat"])
+        assert int(v["elig"][0, h]) == int(want["elig"][0, 0]), (h, stat)
+        # centred keys: exactly the input dtype's rounding of K - mu (GPU mu)
+        kc = v["kc"][0, h]
+        ref = (run.K[0, h].float() - v["mu"][0, h][None, :]).to(kc.dtype)
+        assert torch.equal(kc, ref), h
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_bounds_parity(name):
+    cfg = CONFIGS[name]
+    say("bounds", name)
+    run = Run(cfg).bounds()
+    torch.cuda.synchronize()
+    check_bounds(run)
+
+
+def test_bounds_parity_stress_heads():
+    cfg = CONFIGS["stress"]
+    say("bounds stress")
+    run = Run(cfg).bounds()
+    torch.cuda.synchronize()
+    check_bounds(run, heads=[0, 6, 7, 8, 39])
+    elig = run.views()["elig"][0].cpu().numpy()
+    want = np.array([0 if cfg.is_loose(h) else 1 for h in range(cfg.H)])
+    assert np.array_equal(elig, want)
+
+
+def test_k_is_not_written():
+    cfg = CONFIGS["small"]
+    say("K untouched")
+    run = Run(cfg)
+    before = run.K.clone()
+    run.bounds()
+    run.forward()
+    assert torch.equal(before, run.K)
+
+
+# ------------------------------------------------------------------ forward, full outputs
+
+def test_tiny_fp32_full():
+    cfg = CONFIGS["tiny"]
+    say("forward tiny fp32")
+    run = Run(cfg).bounds()
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    for mode in ("auto", "online", "fixed"):
+        O = run.forward(mode)
+        assert_close(cfg, O, want, f"tiny {mode}")
+
+
+def test_small_bf16_full():
+    cfg = CONFIGS["small"]
+    say("forward small bf16")
+    run = Run(cfg).bounds()
+    O = run.forward("auto")
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    mx, mean = assert_close(cfg, O, want, "small auto")
+    print(f"small auto: max {mx:.3g} mean {mean:.3g}")
+    O2 = run.forward("online")
+    assert_close(cfg, O2, want, "small online")
+
+
+# ------------------------------------------------------------------ forward, full size sampled
+
+@pytest.mark.parametrize("name,heads", [("720p", [0, 11, 23]), ("1080p", [0, 17]),
+                                        ("stress", [6, 7, 33])])
+def test_full_size_sampled(name, heads):
+    cfg = CONFIGS[name]
+    say("forward full size", name)
+    run = Run(cfg).bounds()
+    O = run.forward("auto")
+    assert bool(torch.isfinite(O).all())
+    for h in heads:
+        rows = sample_rows(cfg, 150, seed=h)
+        want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+        mx, mean = assert_close(cfg, O[0, h, rows], want, f"{name} head {h}")
+        print(f"{name} h{h}: max {mx:.3g} mean {mean:.3g}")
+    if name == "stress":
+        v = run.views()
+        assert int(v["elig"][0, 7]) == 0 and int(v["elig"][0, 6]) == 1
+
+
+def test_auto_vs_online_ab():
+    """Fallback heads take the same code path in both modes (bit-identical);
+    eligible heads agree within the bf16 tolerance."""
+    cfg = CONFIGS["stress"].with_(F=6, T=720, H=10, loose_period=5, loose_phase=2)
+    say("auto vs online")
+    run = Run(cfg).bounds()
+    elig = run.views()["elig"][0].cpu().numpy()
+    assert list(np.nonzero(elig == 0)[0]) == [2, 7]
+    Oa = run.forward("auto")
+    Oo = run.forward("online")
+    for h in range(cfg.H):
+        if elig[h]:
+            d = (Oa[0, h].float() - Oo[0, h].float()).abs()
+            assert float(d.max()) <= BF16_MAX_ABS
+        else:
+            assert torch.equal(Oa[0, h], Oo[0, h]), h
+    for h in (2, 3):
+        rows = sample_rows(cfg, 100, seed=h)
+        want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+        assert_close(cfg, Oa[0, h, rows], want, f"ab head {h}")
+
+
+def test_fixed_only_on_a_loose_head_breaks():
+    """Negative control: forcing the fixed max on a loose head underflows."""
+    cfg = CONFIGS["stress"].with_(F=6, T=720, H=3, loose_period=3, loose_phase=1)
+    say("fixed-only negative control")
+    run = Run(cfg).bounds()
+    O = run.forward("fixed")
+    rows = sample_rows(cfg, 100, seed=0)
+    want = oracle_rows(cfg, run.Q, run.K, run.V, 0, 1, rows)
+    mx, _, finite = errors(O[0, 1, rows], want)
+    assert (not finite) or mx > BF16_MAX_ABS
+    want0 = oracle_rows(cfg, run.Q, run.K, run.V, 0, 0, rows)
+    assert_close(cfg, O[0, 0, rows], want0, "fixed-only eligible head")
+
+
+def test_determinism():
+    cfg = CONFIGS["small"]
+    say("determinism")
+    a = Run(cfg).bounds()
+    Oa = a.forward()
+    wa = a.ws.clone()
+    b = Run(cfg).bounds()
+    Ob = b.forward()
+    assert torch.equal(Oa, Ob)
+    assert torch.equal(wa, b.ws)        # every bound product, bit for bit
+
+
+# ------------------------------------------------------------------ probes
+
+def probe_inputs(cfg, q_zero, v_kind, seed=0):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    dt = cfg.torch_dtype
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    Q = torch.zeros(shape, device="cuda", dtype=dt) if q_zero else \
+        torch.randn(shape, generator=g, device="cuda").to(dt)
+    K = (torch.randn(shape, generator=g, device="cuda") + 2.0).to(dt)
+    idx = torch.arange(cfg.N, device="cuda")
+    V = torch.zeros(shape, device="cuda", dtype=dt)
+    if v_kind == "frame":
+        V[:, :, idx, idx // cfg.T] = 1
+    else:
+        V[:, :, idx, (idx // 16) % cfg.d] = 1
+    return Q, K, V
+
+
+@pytest.mark.parametrize("name", ["small", "720p"])
+def test_probe_frame_one_hot(name):
+    """V_j = one-hot(frame of j): weight outside the slice is exactly zero."""
+    cfg = CONFIGS[name].with_(H=2)
+    say("probe frame", name)
+    run = Run(cfg, inputs=probe_inputs(cfg, False, "frame")).bounds()
+    O = run.forward()[0].float().cpu().numpy()
+    frame = np.arange(cfg.N) // cfg.T
+    for f in range(cfg.F):
+        allowed = set(orc.slice_frames(cfg.F, cfg.window, cfg.ref_frame, f))
+        outside = [g for g in range(cfg.F) if g not in allowed]
+        blk = O[:, frame == f]
+        assert np.all(blk[:, :, outside] == 0.0), f
+        assert np.all(np.abs(blk[:, :, :cfg.F].sum(-1) - 1.0) < 2e-2), f
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "720p", "1080p"])
+def test_probe_granule_counts(name):
+    """Q = 0 and V_j = one-hot((j // 16) mod d): every row's output is the
+    share of its slice's 16-key granules in each class, known exactly, so a
+    dropped or doubled granule shows up far above bf16 rounding."""
+    cfg = CONFIGS[name].with_(H=1)
+    say("probe granules", name)
+    run = Run(cfg, inputs=probe_inputs(cfg, True, "granule")).bounds()
+    O = run.forward()[0, 0].double().cpu().numpy()
+    for f in range(cfg.F):
+        keys = orc.slice_keys(cfg.F, cfg.T, cfg.window, cfg.ref_frame, f)
+        want = np.bincount((keys // 16) % cfg.d, minlength=cfg.d) / keys.size
+        got = O[f * cfg.T:(f + 1) * cfg.T]
+        tol = 4e-3 * want.max() if cfg.dtype == "bf16" else 1e-6
+        assert np.max(np.abs(got - want[None, :])) <= tol, f
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # name, F, T, H, d, dtype, window, ref
+    ("one-frame", 1, 64, 2, 128, "bf16", 0, 0),
+    ("one-granule-frames", 6, 16, 2, 128, "bf16", 1, 0),
+    ("window-0-mid-ref", 7, 48, 2, 128, "bf16", 0, 3),
+    ("ref-last", 9, 96, 2, 128, "bf16", 1, 8),
+    ("ref-adjacent", 6, 80, 1, 128, "bf16", 1, 3),
+    ("full-window", 5, 96, 2, 128, "bf16", 4, 2),
+    ("d64-bf16", 5, 240, 3, 64, "bf16", 1, 0),
+    ("d128-f32", 4, 32, 2, 128, "f32", 1, 0),
+    ("ragged-tails", 5, 880, 2, 128, "bf16", 2, 4),
+    ("max-frames", 255, 16, 1, 128, "bf16", 2, 100),
+    ("batch-2", 4, 144, 3, 128, "bf16", 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(case):
+    name, F, T, H, d, dt, w, r = case
+    cfg = CONFIGS["small"].with_(name=name, F=F, T=T, H=H, d=d, dtype=dt, window=w,
+                                 ref_frame=r, B=2 if name == "batch-2" else 1)
+    say("edge", case)
+    run = Run(cfg).bounds()
+    O = run.forward()
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    assert_close(cfg, O, want, name)
+    O2 = run.forward("online")
+    assert_close(cfg, O2, want, name + " online")
+
+
+@pytest.mark.parametrize("bq", [16, 48, 80, 176])
+def test_block_size_choices_small(bq):
+    """Every valid q-block size gives the same answer within tolerance."""
+    cfg = CONFIGS["small"].with_(H=2, T=880 if bq != 48 else 960)
+    say("bq", bq)
+    run = Run(cfg, bq=bq).bounds()
+    O = run.forward()
+    rows = sample_rows(cfg, 200, seed=bq)
+    for h in range(cfg.H):
+        want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+        assert_close(cfg, O[0, h, rows], want, f"bq {bq} head {h}")
+
+
+def test_attention_entry_point():
+    cfg = CONFIGS["small"].with_(H=4)
+    say("fsa_attention")
+    run = Run(cfg)
+    O = fsa.attention(run.Q, run.K, run.V, cfg.F, cfg.T, cfg.window, cfg.ref_frame)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, 100, seed=1)
+    want = oracle_rows(cfg, run.Q, run.K, run.V, 0, 3, rows)
+    assert_close(cfg, O[0, 3, rows], want, "fsa_attention")
+    run.bounds()
+    assert torch.equal(run.forward(), O)
