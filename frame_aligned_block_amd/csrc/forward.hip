@@ -99,16 +99,243 @@ __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh) {
     return p.elig[bh] != 0;
 }
 
-// Position, within a 32-key group of the transposed V tile, of the 4-key
-// group a (keys 4a..4a+3): lane group j of the P.V MFMA holds keys 4j..4j+3
-// (slots 0-3) and 16+4j..16+4j+3 (slots 4-7) of the group.
-__device__ __forceinline__ int vt_pos(int a) { return a < 4 ? 8 * a : 8 * (a - 4) + 4; }
+// ---------------------------------------------------------------- bf16 route
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
+constexpr int kBK = 64;          // keys per LDS chunk
+constexpr int kStages = 4;       // LDS ring: chunks c .. c+3 in flight
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <int D>
+struct Geo {
+    static constexpr int KS = D / 32;                  // k-steps of S^T over d
+    static constexpr int DB = D / 16;                  // 16-wide column blocks of O^T
+    static constexpr int SEGS = D / 8;                 // 16-byte segments per key row
+    static constexpr int ROWB = 2 * D;                 // bytes per key row
+    static constexpr int TILE = kBK * ROWB;            // one K (or V) chunk
+    static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
+    static constexpr int RPI = 64 / SEGS;              // rows one 1 KB wave load moves
+    static constexpr int NI = kBK / (RPI * fsa::kWaves);   // wave loads per tile
+    static constexpr int LOADS = 2 * NI;               // wave loads per chunk
+};
+
+// XOR swizzles of the 16-byte segments of key row R (rows are unpadded
+// because the direct-to-LDS loads write 1 KB linearly): K rows are read 16 at
+// a time at one segment, V rows 4 at a time with the transposing read; both
+// patterns then touch 64 distinct banks per 16-lane pass.
+template <int D>
+__device__ __forceinline__ int kswz(int R) { return D == 128 ? (R & 15) : ((R >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int R) { return D == 128 ? 2 * (R & 7) : 2 * ((R >> 1) & 3); }
+
+// vmcnt(n) with no wait on the other counters (gfx9 encoding).
+#define FSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Start the asynchronous global -> LDS copy of chunk ch of the slice walk
+// (K and V rows straight into the stage, no registers). Positions past the
+// slice are clamped to its last key: harmless duplicates never read.
+template <int D>
+__device__ __forceinline__ void issue_chunk(unsigned char* stage, const Slice& sl, const __bf16* Kh,
+                                            const __bf16* Vh, int ch, int wave, int lane) {
+    using GG = Geo<D>;
+#if defined(__HIP_DEVICE_COMPILE__)   // LDS-address-space builtins exist only in the device pass
+    const int s = lane % GG::SEGS;
+#pragma unroll
+    for (int i = 0; i < GG::NI; ++i) {
+        const int blk = wave * GG::NI + i;
+        const int R = blk * GG::RPI + lane / GG::SEGS;
+        const size_t key = size_t(sl.key(min(ch * kBK + R, sl.total - 1)));
+        __builtin_amdgcn_global_load_lds(Kh + key * D + 8 * (s ^ kswz<D>(R)),
+                                         (lds_void*)(stage + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Vh + key * D + 8 * (s ^ vswz<D>(R)),
+                                         (lds_void*)(stage + GG::TILE + blk * 1024), 16, 0, 0);
+    }
+#endif
 }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
+
+// S^T for the 32 keys at chunk-local key koff (0 or 32): s[0] = first 16 keys,
+// s[1] = next 16; the lane holds query ln of each granule and keys 4lj..4lj+3.
+template <int D, int G, int NB>
+__device__ __forceinline__ void scores(const unsigned char* Ks, int koff,
+                                       const bf16x8 (&qf)[G][D / 32], f32x4 (&s)[2][G], int ln,
+                                       int lj) {
+    using GG = Geo<D>;
+    const int sw = kswz<D>(ln);                  // koff is a multiple of 16
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < GG::KS; ++ks) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                Ks + (koff + 16 * b + ln) * GG::ROWB + 16 * ((4 * ks + lj) ^ sw));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                s[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[g][ks], s[b][g], 0, 0, 0);
+        }
+    }
+}
+
+// V^T operand for column block db and key block b of the 32 keys at koff:
+// four keys 4lj..4lj+3 (+16b) of column 16db+ln, read transposed out of
+// row-major V (each lane fetches 4 columns of one key row).
+template <int D>
+__device__ __forceinline__ bf16x4 v_operand(const unsigned char* Vs, int koff, int b, int db,
+                                            int vrow, int vsw, int ln) {
+    using GG = Geo<D>;
+    const int seg = (2 * db + ((ln & 3) >> 1)) ^ vsw;
+    const unsigned char* a = Vs + (koff + 16 * b) * GG::ROWB + vrow + 16 * seg;
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
+#else
+    return bf16x4{};
+#endif
+}
+
+// Probabilities of NK scores of one granule-row. Fixed route: the shift is
+// the row's Cauchy-Schwarz bound. Online route: the running max, with the
+// accumulator and row sum rescaled when it grows.
+template <int D, int G, bool FIXED, int NK>
+__device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const float (&shift)[G],
+                                      float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
+                                      float (&p)[NK]) {
+    if (FIXED) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -shift[g]));
+    } else {
+        float mx = sv[0][0];
+#pragma unroll
+        for (int i = 1; i < NK; ++i) mx = fmaxf(mx, sv[i >> 2][i & 3]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m[g] - mnew) * c);
+        m[g] = mnew;
+        rs[g] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[g][db] *= alpha;
+        const float sh = mnew * c;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -sh));
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NK; i += 2) t += p[i] + p[i + 1];
+    rs[g] += t;
+}
+
+// Softmax and O^T += V^T P^T for the 32 keys at koff (NB = 2) or the lone
+// 16-key granule at koff (NB = 1, K = 16 products).
+template <int D, int G, bool FIXED, int NB>
+__device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const f32x4 (&s)[2][G],
+                                        float c, const float (&shift)[G], float (&m)[G],
+                                        float (&rs)[G], f32x4 (&o)[G][D / 16], int vrow, int vsw,
+                                        int ln) {
+    using GG = Geo<D>;
+    if (NB == 2) {
+        bf16x8 pk[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const f32x4 sv[2] = {s[0][g], s[1][g]};
+            float p[8];
+            probs<D, G, FIXED, 8>(sv, g, c, shift, m, rs, o, p);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pk[g][i] = __bf16(p[i]);
+        }
+#pragma unroll
+        for (int db = 0; db < GG::DB; ++db) {
+            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, vrow, vsw, ln);
+            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, vrow, vsw, ln);
+            const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[g], o[g][db], 0, 0, 0);
+        }
+    } else {
+        i16x4 pk[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const f32x4 sv[1] = {s[0][g]};
+            float p[4];
+            probs<D, G, FIXED, 4>(sv, g, c, shift, m, rs, o, p);
+            const bf16x4 b = {__bf16(p[0]), __bf16(p[1]), __bf16(p[2]), __bf16(p[3])};
+            pk[g] = __builtin_bit_cast(i16x4, b);
+        }
+#pragma unroll
+        for (int db = 0; db < GG::DB; ++db) {
+            const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, vrow, vsw, ln));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[g], o[g][db], 0, 0, 0);
+        }
+    }
+}
+
+// The slice walk of one workgroup. Chunks of 64 keys stream into a 4-stage
+// LDS ring by direct-to-LDS loads issued three chunks ahead; a chunk is
+// waited for (vmcnt) two chunks after its loads were issued, then one barrier
+// publishes it. Each wave computes S^T one 32-key step ahead of the softmax
+// and P.V of the current step, so neighbouring steps' matrix and vector work
+// are independent and can interleave.
+template <int D, int G, bool FIXED>
+__device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
+                                       const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
+                                       const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
+                                       float (&rs)[G], int wave, int lane) {
+    using GG = Geo<D>;
+    const int ln = lane & 15, lj = lane >> 4;
+    const int nfull = sl.total >> 5;              // whole 32-key steps
+    const bool lone = (sl.total & 16) != 0;       // a final 16-key granule
+    // per-lane constants of the transposing V read
+    const int vr = 4 * lj + (ln >> 2);
+    const int vrow = vr * GG::ROWB + 8 * (ln & 1);
+    const int vsw = vswz<D>(vr);
+    float m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+
+#pragma unroll
+    for (int ch = 0; ch < kStages - 1; ++ch)
+        issue_chunk<D>(smem + ch * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
+    FSA_WAIT_VMCNT(GG::LOADS);                    // chunks 0 and 1 have landed
+    __builtin_amdgcn_s_barrier();
+
+    f32x4 sA[2][G], sB[2][G];
+    if (nfull > 0) scores<D, G, 2>(smem, 0, qf, sA, ln, lj);
+
+    // steady state: chunk ch with steps 2ch, 2ch+1 and the look-ahead 2ch+2 all whole
+    const int steady = nfull >= 3 ? (nfull - 1) / 2 : 0;
+    for (int ch = 0; ch < steady; ++ch) {
+        const unsigned char* S0 = smem + (ch & 3) * GG::STAGE;
+        const unsigned char* S1 = smem + ((ch + 1) & 3) * GG::STAGE;
+        issue_chunk<D>(smem + ((ch + 3) & 3) * GG::STAGE, sl, Kh, Vh, ch + 3, wave, lane);
+        scores<D, G, 2>(S0, 32, qf, sB, ln, lj);
+        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sA, c, shift, m, rs, o, vrow, vsw, ln);
+        scores<D, G, 2>(S1, 0, qf, sA, ln, lj);
+        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sB, c, shift, m, rs, o, vrow, vsw, ln);
+        FSA_WAIT_VMCNT(GG::LOADS);                // chunk ch+2 has landed
+        __builtin_amdgcn_s_barrier();
+    }
+    // the last whole steps: chunk `steady` (resident; sA holds its first step)
+    const unsigned char* S0 = smem + (steady & 3) * GG::STAGE;
+    if (2 * steady < nfull) {
+        const bool two = 2 * steady + 1 < nfull;
+        if (two) scores<D, G, 2>(S0, 32, qf, sB, ln, lj);
+        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sA, c, shift, m, rs, o, vrow, vsw, ln);
+        if (two) pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sB, c, shift, m, rs, o, vrow, vsw, ln);
+    }
+    if (lone) {                                   // in chunk `steady` or `steady + 1`, resident
+        const int kofs = 32 * nfull;
+        const unsigned char* SL = smem + ((kofs >> 6) & 3) * GG::STAGE;
+        const int koff = kofs & (kBK - 1);
+        scores<D, G, 1>(SL, koff, qf, sA, ln, lj);
+        pv_step<D, G, FIXED, 1>(SL + GG::TILE, koff, sA, c, shift, m, rs, o, vrow, vsw, ln);
+    }
+    FSA_WAIT_VMCNT(0);                            // no copy may outlive the workgroup
 }
 
 // Workgroups per CU the register budget allows: two (<= 256 VGPRs per lane)
@@ -117,18 +344,8 @@ constexpr int fwd_occupancy(int D, int G) { return D == 128 ? (G <= 2 ? 2 : 1) :
 
 template <int D, int G>
 __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {
-    constexpr int KS = D / 32;          // k-steps of S^T over d
-    constexpr int DB = D / 16;          // 16-wide column blocks of O^T
-    constexpr int BK = 64;              // keys per chunk
-    constexpr int KROW = D * 2 + 16;    // bytes per K row in LDS (padded)
-    constexpr int VROW = BK * 2 + 16;   // bytes per V^T row in LDS (padded)
-    constexpr int KBYTES = BK * KROW;
-    constexpr int STAGE = KBYTES + D * VROW;
-    constexpr int KV16 = D / 8;         // 16-byte pieces per row
-    constexpr int KPASS = BK * KV16 / fsa::kThreads;
-    constexpr int KROWS_PER_PASS = fsa::kThreads / KV16;
-    constexpr int VTASKS = (BK / 4) * KV16;   // (4 keys x 8 columns) tasks
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    using GG = Geo<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * GG::STAGE];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
@@ -140,7 +357,6 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const int bh = t1 / p.F;
     const int T = p.T;
     const Slice sl = slice_of(p.tab, f, T);
-    const int nchunks = (sl.total + BK - 1) / BK;
 
     const size_t base = size_t(bh) * p.N * D;
     const __bf16* Qh = static_cast<const __bf16*>(p.Q) + base;
@@ -149,189 +365,33 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const __bf16* Vh = static_cast<const __bf16*>(p.V) + base;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
 
+    // A wave past the frame's last row unit repeats that unit (its SIMD would
+    // idle anyway) and stores nothing: no divergent branch in the loop.
     const int unit = gq * fsa::kWaves + wave;
-    const bool active = unit < p.units_per_frame;       // uniform per wave
-    const int row0 = f * T + unit * 16 * G;
+    const bool active = unit < p.units_per_frame;
+    const int row0 = f * T + min(unit, p.units_per_frame - 1) * 16 * G;
     const float c = p.c;
 
-    bf16x8 qf[G][KS];
-    float shift[G], mrun[G], rs[G];
-    f32x4 o[G][DB];
+    bf16x8 qf[G][GG::KS];
+    float shift[G], rs[G];
+    f32x4 o[G][GG::DB];
+    const float rsl = p.rslice[size_t(bh) * p.F + f];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+        const int row = row0 + 16 * g + ln;
+#pragma unroll
+        for (int ks = 0; ks < GG::KS; ++ks)
+            qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
+        shift[g] = c * (p.qnorm[size_t(bh) * p.N + row] * rsl);
         rs[g] = 0.f;
-        mrun[g] = -INFINITY;
-        shift[g] = 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if (active) {
-        const float rsl = p.rslice[size_t(bh) * p.F + f];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int row = row0 + 16 * g + ln;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
-            shift[g] = c * (p.qnorm[size_t(bh) * p.N + row] * rsl);
-        }
+        for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- chunk staging: global -> registers -> LDS
-    uint4 kreg[KPASS];
-    uint4 vreg[4];
-    const int kcol = tid % KV16;
-    const int krow = tid / KV16;
-    const bool vtask = tid < VTASKS;
-    const int vdg = tid % KV16, vkg = tid / KV16;
-
-    auto load_chunk = [&](int ch) {
-        const int x0 = ch * BK;
-#pragma unroll
-        for (int ps = 0; ps < KPASS; ++ps) {
-            const int x = x0 + ps * KROWS_PER_PASS + krow;
-            kreg[ps] = x < sl.total
-                           ? *reinterpret_cast<const uint4*>(Kh + size_t(sl.key(x)) * D + 8 * kcol)
-                           : uint4{0, 0, 0, 0};
-        }
-        if (vtask) {
-            const int x = x0 + 4 * vkg;
-            if (x < sl.total) {
-                const int k0 = sl.key(x);       // 4-key groups never cross a run
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vreg[i] = *reinterpret_cast<const uint4*>(Vh + size_t(k0 + i) * D + 8 * vdg);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vreg[i] = uint4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_chunk = [&](int st) {
-        unsigned char* Ks = smem + st * STAGE;
-        unsigned char* Vs = Ks + KBYTES;
-#pragma unroll
-        for (int ps = 0; ps < KPASS; ++ps)
-            *reinterpret_cast<uint4*>(Ks + (ps * KROWS_PER_PASS + krow) * KROW + 16 * kcol) = kreg[ps];
-        if (vtask) {
-            const int col = 2 * (32 * (vkg >> 3) + vt_pos(vkg & 7));
-            const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-            const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-            const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-            const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                uint2 lo = {lo_pair(v0[w], v1[w]), lo_pair(v2[w], v3[w])};
-                uint2 hi = {hi_pair(v0[w], v1[w]), hi_pair(v2[w], v3[w])};
-                *reinterpret_cast<uint2*>(Vs + (8 * vdg + 2 * w) * VROW + col) = lo;
-                *reinterpret_cast<uint2*>(Vs + (8 * vdg + 2 * w + 1) * VROW + col) = hi;
-            }
-        }
-    };
-
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int st = ch & 1;
-        const bool more = ch + 1 < nchunks;
-        if (more) load_chunk(ch + 1);
-        if (active) {
-            const unsigned char* Ks = smem + st * STAGE;
-            const unsigned char* Vs = Ks + KBYTES;
-            const int nb = min(4, (sl.total - ch * BK) >> 4);     // 16-key granules
-#pragma unroll
-            for (int step = 0; step < 2; ++step) {
-                const int kb0 = 2 * step;
-                if (kb0 >= nb) break;
-                const bool two = kb0 + 1 < nb;
-                f32x4 sa[G], sb[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    sa[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    sb[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(
-                        Ks + (16 * kb0 + ln) * KROW + 64 * ks + 16 * lj);
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        sa[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[g][ks], sa[g], 0, 0, 0);
-                    if (two) {
-                        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(
-                            Ks + (16 * kb0 + 16 + ln) * KROW + 64 * ks + 16 * lj);
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            sb[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[g][ks], sb[g], 0, 0, 0);
-                    }
-                }
-                bf16x8 pk[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float pa[4], pb[4];
-                    if (fixed) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pa[i] = __builtin_amdgcn_exp2f(fmaf(sa[g][i], c, -shift[g]));
-                            pb[i] = two ? __builtin_amdgcn_exp2f(fmaf(sb[g][i], c, -shift[g])) : 0.f;
-                        }
-                    } else {
-                        float mx = fmaxf(fmaxf(sa[g][0], sa[g][1]), fmaxf(sa[g][2], sa[g][3]));
-                        if (two)
-                            mx = fmaxf(mx, fmaxf(fmaxf(sb[g][0], sb[g][1]), fmaxf(sb[g][2], sb[g][3])));
-                        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                        const float mnew = fmaxf(mrun[g], mx);
-                        const float alpha = __builtin_amdgcn_exp2f((mrun[g] - mnew) * c);
-                        mrun[g] = mnew;
-                        rs[g] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < DB; ++db) o[g][db] *= alpha;
-                        const float sh = mnew * c;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pa[i] = __builtin_amdgcn_exp2f(fmaf(sa[g][i], c, -sh));
-                            pb[i] = two ? __builtin_amdgcn_exp2f(fmaf(sb[g][i], c, -sh)) : 0.f;
-                        }
-                    }
-                    rs[g] += (pa[0] + pa[1]) + (pa[2] + pa[3]);
-                    if (two) rs[g] += (pb[0] + pb[1]) + (pb[2] + pb[3]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pk[g][i] = __bf16(pa[i]);
-                        pk[g][4 + i] = __bf16(pb[i]);
-                    }
-                }
-                if (two) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-                            Vs + (16 * db + ln) * VROW + 64 * step + 16 * lj);
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[g], o[g][db], 0, 0, 0);
-                    }
-                } else {
-                    // a lone 16-key granule: K = 16 products, operand slots 0-3
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const i16x4 va = *reinterpret_cast<const i16x4*>(
-                            Vs + (16 * db + ln) * VROW + 64 * step + 16 * lj);
-#pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            const bf16x4 p4 = {pk[g][0], pk[g][1], pk[g][2], pk[g][3]};
-                            o[g][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                                va, __builtin_bit_cast(i16x4, p4), o[g][db], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-        }
-        if (more) store_chunk(st ^ 1);
-        __syncthreads();
-    }
+    if (fixed)
+        attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, wave, lane);
+    else
+        attend<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, wave, lane);
 
     if (!active) return;
 #pragma unroll
@@ -341,7 +401,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
         const float inv = 1.0f / tot;
         const int row = row0 + 16 * g + ln;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < GG::DB; ++db) {
             bf16x4 out;
 #pragma unroll
             for (int i = 0; i < 4; ++i) out[i] = __bf16(o[g][db][i] * inv);
