@@ -34,8 +34,6 @@ def command(out: str = LIB, extra=()) -> list[str]:
         path = os.path.join(CSRC, s)
         # host-only sources are still compiled by the HIP driver, as HIP
         srcs += ["-x", "hip", path]
-    # MFMA accumulators in VGPRs: the softmax reads every score with VALU,
-    # and AGPR-resident scores each cost an extra v_accvgpr_read.
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-mllvm", "-amdgpu-mfma-vgpr-form=1",

@@ -102,66 +102,89 @@ __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh) {
 // ---------------------------------------------------------------- bf16 route
 
 constexpr int kBK = 64;          // keys per LDS chunk
-constexpr int kStages = 4;       // LDS ring: chunks c .. c+3 in flight
+constexpr int kStages = 2;       // LDS ring: chunk c+1 lands while c is consumed
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// LDS tiles. A chunk's K (and V) tile is D/32 column sub-tiles of 64 rows x
+// 64 bytes (32 columns each), so every read address is a per-lane constant
+// plus an immediate. Small XOR swizzles keep each read pattern on distinct
+// banks (64 banks x 4 bytes):
+//  * K (read 16 rows at one 16-byte segment): segment ^= (row >> 1) & 3
+//    (chosen by measuring SQ_LDS_BANK_CONFLICT over candidate swizzles);
+//  * V (read transposed, 4 rows x 32 bytes per 16 lanes): 32-byte half
+//    ^= (row >> 2) & 1.
 template <int D>
 struct Geo {
-    static constexpr int KS = D / 32;                  // k-steps of S^T over d
+    static constexpr int KS = D / 32;                  // k-steps of S^T over d = sub-tiles
     static constexpr int DB = D / 16;                  // 16-wide column blocks of O^T
-    static constexpr int SEGS = D / 8;                 // 16-byte segments per key row
-    static constexpr int ROWB = 2 * D;                 // bytes per key row
-    static constexpr int TILE = kBK * ROWB;            // one K (or V) chunk
+    static constexpr int SUB = kBK * 64;               // one 64 x 64-byte sub-tile
+    static constexpr int TILE = KS * SUB;              // one K (or V) chunk
     static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
-    static constexpr int RPI = 64 / SEGS;              // rows one 1 KB wave load moves
-    static constexpr int NI = kBK / (RPI * fsa::kWaves);   // wave loads per tile
-    static constexpr int LOADS = 2 * NI;               // wave loads per chunk
+    static constexpr int LOADS = 2 * KS;               // wave loads (1 KB each) per chunk
 };
-
-// XOR swizzles of the 16-byte segments of key row R (rows are unpadded
-// because the direct-to-LDS loads write 1 KB linearly): K rows are read 16 at
-// a time at one segment, V rows 4 at a time with the transposing read; both
-// patterns then touch 64 distinct banks per 16-lane pass.
-template <int D>
-__device__ __forceinline__ int kswz(int R) { return D == 128 ? (R & 15) : ((R >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int vswz(int R) { return D == 128 ? 2 * (R & 7) : 2 * ((R >> 1) & 3); }
 
 // vmcnt(n) with no wait on the other counters (gfx9 encoding).
 #define FSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// Start the asynchronous global -> LDS copy of chunk ch of the slice walk
-// (K and V rows straight into the stage, no registers). Positions past the
-// slice are clamped to its last key: harmless duplicates never read.
+// One 16-byte-per-lane direct global -> LDS copy: 64 lanes fill 1 KB of LDS
+// at `lds` (wave-uniform) from gbase + voff. Written as inline assembly on
+// purpose: the compiler's wait-count pass otherwise assumes such a copy may
+// alias every later LDS read and stalls each chunk on vmcnt(0) until the copy
+// issued for three chunks ahead has landed. Completion is tracked explicitly
+// (FSA_WAIT_VMCNT) before the barrier that publishes a chunk. M0 is a
+// reserved register the compiler never keeps values in.
+__device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsigned voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
+}
+
+// Start the asynchronous global -> LDS copy of chunk ch of the slice walk (K
+// and V straight into the stage, no registers). Wave w moves rows 16w..16w+15
+// of every sub-tile; lane l carries row 16w + l/4, 16-byte segment l%4.
+// Positions past the slice are clamped to its last key: harmless duplicates
+// that are never read.
 template <int D>
-__device__ __forceinline__ void issue_chunk(unsigned char* stage, const Slice& sl, const __bf16* Kh,
+__device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                             const __bf16* Vh, int ch, int wave, int lane) {
     using GG = Geo<D>;
-#if defined(__HIP_DEVICE_COMPILE__)   // LDS-address-space builtins exist only in the device pass
-    const int s = lane % GG::SEGS;
+    const int row = 16 * wave + (lane >> 2);
+    const unsigned rowoff = unsigned(sl.key(min(ch * kBK + row, sl.total - 1))) * (2 * D);
+    const int seg = lane & 3;
+    const unsigned koff = rowoff + 16 * (seg ^ ((lane >> 3) & 3));     // (row >> 1) & 3
+    const unsigned voff = rowoff + 16 * (seg ^ (((lane >> 4) & 1) << 1));
 #pragma unroll
-    for (int i = 0; i < GG::NI; ++i) {
-        const int blk = wave * GG::NI + i;
-        const int R = blk * GG::RPI + lane / GG::SEGS;
-        const size_t key = size_t(sl.key(min(ch * kBK + R, sl.total - 1)));
-        __builtin_amdgcn_global_load_lds(Kh + key * D + 8 * (s ^ kswz<D>(R)),
-                                         (lds_void*)(stage + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(Vh + key * D + 8 * (s ^ vswz<D>(R)),
-                                         (lds_void*)(stage + GG::TILE + blk * 1024), 16, 0, 0);
+    for (int i = 0; i < GG::KS; ++i) {
+        const unsigned dst = stage_lds + i * GG::SUB + wave * 1024;
+        lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * i, koff);
+        lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * i, voff);
     }
-#endif
+}
+
+// Per-lane LDS byte offsets (constant for the whole walk).
+struct LaneAddr {
+    int k;        // K read: row ln, segment lj (swizzled)
+    int v0, v1;   // V transposed read, even / odd column block
+};
+
+__device__ __forceinline__ LaneAddr lane_addr(int ln, int lj) {
+    LaneAddr a;
+    a.k = ln * 64 + 16 * (lj ^ ((ln >> 1) & 3));
+    const int vbase = (4 * lj + (ln >> 2)) * 64 + 8 * (ln & 3);
+    a.v0 = vbase + 32 * (lj & 1);
+    a.v1 = vbase + 32 * ((lj & 1) ^ 1);
+    return a;
 }
 
 // S^T for the 32 keys at chunk-local key koff (0 or 32): s[0] = first 16 keys,
 // s[1] = next 16; the lane holds query ln of each granule and keys 4lj..4lj+3.
 template <int D, int G, int NB>
 __device__ __forceinline__ void scores(const unsigned char* Ks, int koff,
-                                       const bf16x8 (&qf)[G][D / 32], f32x4 (&s)[2][G], int ln,
-                                       int lj) {
+                                       const bf16x8 (&qf)[G][D / 32], f32x4 (&s)[2][G],
+                                       const LaneAddr& la) {
     using GG = Geo<D>;
-    const int sw = kswz<D>(ln);                  // koff is a multiple of 16
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -171,7 +194,7 @@ __device__ __forceinline__ void scores(const unsigned char* Ks, int koff,
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                Ks + (koff + 16 * b + ln) * GG::ROWB + 16 * ((4 * ks + lj) ^ sw));
+                Ks + ks * GG::SUB + (koff + 16 * b) * 64 + la.k);
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 s[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[g][ks], s[b][g], 0, 0, 0);
@@ -180,19 +203,27 @@ __device__ __forceinline__ void scores(const unsigned char* Ks, int koff,
 }
 
 // V^T operand for column block db and key block b of the 32 keys at koff:
-// four keys 4lj..4lj+3 (+16b) of column 16db+ln, read transposed out of
-// row-major V (each lane fetches 4 columns of one key row).
+// keys 4lj..4lj+3 (+16b) of column 16db+ln, read transposed out of row-major
+// V (each lane fetches 4 columns of one key row).
 template <int D>
 __device__ __forceinline__ bf16x4 v_operand(const unsigned char* Vs, int koff, int b, int db,
-                                            int vrow, int vsw, int ln) {
+                                            const LaneAddr& la) {
     using GG = Geo<D>;
-    const int seg = (2 * db + ((ln & 3) >> 1)) ^ vsw;
-    const unsigned char* a = Vs + (koff + 16 * b) * GG::ROWB + vrow + 16 * seg;
+    const unsigned char* a = Vs + (db >> 1) * GG::SUB + (koff + 16 * b) * 64 + ((db & 1) ? la.v1 : la.v0);
 #if defined(__HIP_DEVICE_COMPILE__)
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a);
 #else
+    (void)a;
     return bf16x4{};
 #endif
+}
+
+// Row sum of packed bf16 probabilities: two terms per v_dot2 (fp32 accumulate).
+__device__ __forceinline__ float sum_pairs(const bf16x2* pp, int n, float acc) {
+    const bf16x2 one = {__bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+    for (int i = 0; i < n; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(pp[i], one, acc, false);
+    return acc;
 }
 
 // Probabilities of NK scores of one granule-row. Fixed route: the shift is
@@ -222,19 +253,16 @@ __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const flo
 #pragma unroll
         for (int i = 0; i < NK; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -sh));
     }
-    float t = 0.f;
-#pragma unroll
-    for (int i = 0; i < NK; i += 2) t += p[i] + p[i + 1];
-    rs[g] += t;
 }
 
 // Softmax and O^T += V^T P^T for the 32 keys at koff (NB = 2) or the lone
-// 16-key granule at koff (NB = 1, K = 16 products).
+// 16-key granule at koff (NB = 1, K = 16 products). The row sum adds the
+// bf16-rounded probabilities, the same values the product consumes.
 template <int D, int G, bool FIXED, int NB>
 __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const f32x4 (&s)[2][G],
                                         float c, const float (&shift)[G], float (&m)[G],
-                                        float (&rs)[G], f32x4 (&o)[G][D / 16], int vrow, int vsw,
-                                        int ln) {
+                                        float (&rs)[G], f32x4 (&o)[G][D / 16],
+                                        const LaneAddr& la) {
     using GG = Geo<D>;
     if (NB == 2) {
         bf16x8 pk[G];
@@ -243,13 +271,16 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
             const f32x4 sv[2] = {s[0][g], s[1][g]};
             float p[8];
             probs<D, G, FIXED, 8>(sv, g, c, shift, m, rs, o, p);
+            bf16x2 pp[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pk[g][i] = __bf16(p[i]);
+            for (int i = 0; i < 4; ++i) pp[i] = bf16x2{__bf16(p[2 * i]), __bf16(p[2 * i + 1])};
+            rs[g] = sum_pairs(pp, 4, rs[g]);
+            pk[g] = bf16x8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
         }
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) {
-            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, vrow, vsw, ln);
-            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, vrow, vsw, ln);
+            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, la);
+            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, la);
             const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
             for (int g = 0; g < G; ++g)
@@ -262,12 +293,14 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
             const f32x4 sv[1] = {s[0][g]};
             float p[4];
             probs<D, G, FIXED, 4>(sv, g, c, shift, m, rs, o, p);
-            const bf16x4 b = {__bf16(p[0]), __bf16(p[1]), __bf16(p[2]), __bf16(p[3])};
-            pk[g] = __builtin_bit_cast(i16x4, b);
+            bf16x2 pp[2] = {bf16x2{__bf16(p[0]), __bf16(p[1])}, bf16x2{__bf16(p[2]), __bf16(p[3])}};
+            rs[g] = sum_pairs(pp, 2, rs[g]);
+            const bf16x4 b4 = {pp[0][0], pp[0][1], pp[1][0], pp[1][1]};
+            pk[g] = __builtin_bit_cast(i16x4, b4);
         }
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) {
-            const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, vrow, vsw, ln));
+            const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, la));
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 o[g][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[g], o[g][db], 0, 0, 0);
@@ -275,72 +308,59 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
     }
 }
 
-// The slice walk of one workgroup. Chunks of 64 keys stream into a 4-stage
-// LDS ring by direct-to-LDS loads issued three chunks ahead; a chunk is
-// waited for (vmcnt) two chunks after its loads were issued, then one barrier
-// publishes it. Each wave computes S^T one 32-key step ahead of the softmax
-// and P.V of the current step, so neighbouring steps' matrix and vector work
-// are independent and can interleave.
+// The slice walk of one workgroup. Chunks of 64 keys stream into a 2-stage
+// LDS ring by direct-to-LDS loads issued one chunk ahead; each chunk is
+// waited for (vmcnt) and published by one barrier. Per 32-key step a wave
+// computes S^T, its softmax and P.V in sequence; two workgroups share each CU
+// (two waves per SIMD), so one wave's matrix work overlaps the other's vector
+// work in hardware.
 template <int D, int G, bool FIXED>
 __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
                                        const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
                                        float (&rs)[G], int wave, int lane) {
     using GG = Geo<D>;
-    const int ln = lane & 15, lj = lane >> 4;
-    const int nfull = sl.total >> 5;              // whole 32-key steps
-    const bool lone = (sl.total & 16) != 0;       // a final 16-key granule
-    // per-lane constants of the transposing V read
-    const int vr = 4 * lj + (ln >> 2);
-    const int vrow = vr * GG::ROWB + 8 * (ln & 1);
-    const int vsw = vswz<D>(vr);
+    const LaneAddr la = lane_addr(lane & 15, lane >> 4);
+    const int nchunks = (sl.total + kBK - 1) / kBK;
     float m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
 
-#pragma unroll
-    for (int ch = 0; ch < kStages - 1; ++ch)
-        issue_chunk<D>(smem + ch * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
-    FSA_WAIT_VMCNT(GG::LOADS);                    // chunks 0 and 1 have landed
+    const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
+    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    FSA_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
 
-    f32x4 sA[2][G], sB[2][G];
-    if (nfull > 0) scores<D, G, 2>(smem, 0, qf, sA, ln, lj);
-
-    // steady state: chunk ch with steps 2ch, 2ch+1 and the look-ahead 2ch+2 all whole
-    const int steady = nfull >= 3 ? (nfull - 1) / 2 : 0;
-    for (int ch = 0; ch < steady; ++ch) {
-        const unsigned char* S0 = smem + (ch & 3) * GG::STAGE;
-        const unsigned char* S1 = smem + ((ch + 1) & 3) * GG::STAGE;
-        issue_chunk<D>(smem + ((ch + 3) & 3) * GG::STAGE, sl, Kh, Vh, ch + 3, wave, lane);
-        scores<D, G, 2>(S0, 32, qf, sB, ln, lj);
-        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sA, c, shift, m, rs, o, vrow, vsw, ln);
-        scores<D, G, 2>(S1, 0, qf, sA, ln, lj);
-        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sB, c, shift, m, rs, o, vrow, vsw, ln);
-        FSA_WAIT_VMCNT(GG::LOADS);                // chunk ch+2 has landed
+    f32x4 sv[2][G];
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const unsigned char* S0 = smem + (ch & 1) * GG::STAGE;
+        if (ch + 1 < nchunks)
+            issue_chunk<D>(smem_lds + ((ch + 1) & 1) * GG::STAGE, sl, Kh, Vh, ch + 1, wave, lane);
+        const int left = sl.total - ch * kBK;        // keys left, a multiple of 16
+        if (left >= kBK) {
+            scores<D, G, 2>(S0, 0, qf, sv, la);
+            pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sv, c, shift, m, rs, o, la);
+            scores<D, G, 2>(S0, 32, qf, sv, la);
+            pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sv, c, shift, m, rs, o, la);
+        } else {                                     // the final chunk: 16, 32 or 48 keys
+            if (left >= 32) {
+                scores<D, G, 2>(S0, 0, qf, sv, la);
+                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sv, c, shift, m, rs, o, la);
+            }
+            if (left & 16) {
+                const int koff = left & 32;
+                scores<D, G, 1>(S0, koff, qf, sv, la);
+                pv_step<D, G, FIXED, 1>(S0 + GG::TILE, koff, sv, c, shift, m, rs, o, la);
+            }
+        }
+        FSA_WAIT_VMCNT(0);                           // chunk ch+1 has landed
         __builtin_amdgcn_s_barrier();
     }
-    // the last whole steps: chunk `steady` (resident; sA holds its first step)
-    const unsigned char* S0 = smem + (steady & 3) * GG::STAGE;
-    if (2 * steady < nfull) {
-        const bool two = 2 * steady + 1 < nfull;
-        if (two) scores<D, G, 2>(S0, 32, qf, sB, ln, lj);
-        pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sA, c, shift, m, rs, o, vrow, vsw, ln);
-        if (two) pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sB, c, shift, m, rs, o, vrow, vsw, ln);
-    }
-    if (lone) {                                   // in chunk `steady` or `steady + 1`, resident
-        const int kofs = 32 * nfull;
-        const unsigned char* SL = smem + ((kofs >> 6) & 3) * GG::STAGE;
-        const int koff = kofs & (kBK - 1);
-        scores<D, G, 1>(SL, koff, qf, sA, ln, lj);
-        pv_step<D, G, FIXED, 1>(SL + GG::TILE, koff, sA, c, shift, m, rs, o, vrow, vsw, ln);
-    }
-    FSA_WAIT_VMCNT(0);                            // no copy may outlive the workgroup
 }
 
-// Workgroups per CU the register budget allows: two (<= 256 VGPRs per lane)
-// while the per-wave state stays small, else one (up to 512 VGPRs + AGPRs).
-constexpr int fwd_occupancy(int D, int G) { return D == 128 ? (G <= 2 ? 2 : 1) : (G <= 3 ? 2 : 1); }
+// Workgroups per CU: two (two waves per SIMD, <= 256 registers per lane)
+// while a wave's accumulators and query fragments fit, else one.
+constexpr int fwd_occupancy(int D, int G) { return G * D <= 256 ? 2 : 1; }
 
 template <int D, int G>
 __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {
@@ -365,11 +385,13 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const __bf16* Vh = static_cast<const __bf16*>(p.V) + base;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
 
-    // A wave past the frame's last row unit repeats that unit (its SIMD would
-    // idle anyway) and stores nothing: no divergent branch in the loop.
+    // A wave owns granules unit*G .. unit*G+G-1 of frame f. Granules past the
+    // frame (the tail of a frame whose granule count G does not divide, or a
+    // whole wave past the last unit) repeat the frame's last granule and are
+    // not stored: every wave runs the same loop, with no predicate inside it.
     const int unit = gq * fsa::kWaves + wave;
-    const bool active = unit < p.units_per_frame;
-    const int row0 = f * T + min(unit, p.units_per_frame - 1) * 16 * G;
+    const int ngran = T >> 4;
+    const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
     const float c = p.c;
 
     bf16x8 qf[G][GG::KS];
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const float rsl = p.rslice[size_t(bh) * p.F + f];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int row = row0 + 16 * g + ln;
+        const int row = f * T + 16 * min(unit * G + g, ngran - 1) + ln;
 #pragma unroll
         for (int ks = 0; ks < GG::KS; ++ks)
             qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
@@ -388,18 +410,19 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
         for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
     if (fixed)
-        attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, wave, lane);
+        attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
     else
-        attend<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, wave, lane);
+        attend<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
 
-    if (!active) return;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+        if (g >= nvalid) break;
         float tot = rs[g] + __shfl_xor(rs[g], 16, 64);
         tot += __shfl_xor(tot, 32, 64);
         const float inv = 1.0f / tot;
-        const int row = row0 + 16 * g + ln;
+        const int row = f * T + 16 * (unit * G + g) + ln;
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) {
             bf16x4 out;
@@ -509,23 +532,13 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
         }
         a.nwg = int32_t(p.forward.workgroups);
         const int G = p.forward.granules;
-        if (s.d == 128) {
-            switch (G) {
-                case 1: launch_bf16<128, 1>(a, stream); break;
-                case 2: launch_bf16<128, 2>(a, stream); break;
-                case 3: launch_bf16<128, 3>(a, stream); break;
-                default:
-                    set_error("fsa_forward: %d granules per wave unsupported at d=128", G);
-                    return FSA_ERR_UNSUPPORTED;
-            }
+        if (s.d == 128 && G == 2) {
+            launch_bf16<128, 2>(a, stream);
+        } else if (s.d == 64 && G == 4) {
+            launch_bf16<64, 4>(a, stream);
         } else {
-            switch (G) {
-                case 1: launch_bf16<64, 1>(a, stream); break;
-                case 2: launch_bf16<64, 2>(a, stream); break;
-                case 3: launch_bf16<64, 3>(a, stream); break;
-                case 4: launch_bf16<64, 4>(a, stream); break;
-                default: launch_bf16<64, 5>(a, stream); break;
-            }
+            set_error("fsa_forward: no kernel for d=%d with %d granules per wave", s.d, G);
+            return FSA_ERR_UNSUPPORTED;
         }
     }
     const hipError_t err = hipGetLastError();

@@ -37,7 +37,7 @@ struct BoundsGeometry {
 
 struct ForwardGeometry {
     int32_t granules;          // 16-row granules per wave
-    int32_t units_per_frame;   // T / (16 * granules)
+    int32_t units_per_frame;   // ceil(T / (16 * granules)); the last may be partial
     int32_t groups_per_frame;  // ceil(units_per_frame / kWaves)
     int64_t workgroups;        // B * H * F * groups_per_frame
 };

@@ -23,22 +23,18 @@ bool in_slice(int32_t F, int32_t window, int32_t ref, int32_t f, int32_t g) {
     return d <= window || g == ref;
 }
 
-// 16-row granules per wave of the forward kernel: the first count in the
-// preferred order that divides the granules available (span / 16). Three
-// (48 rows per wave) divides both 3600/16 = 225 and 8160/16 = 510. With
-// d = 128 more than three granules do not fit the register file.
-int32_t pick_granules(int32_t granules_available, int32_t d) {
-    static const int32_t pref128[] = {3, 2, 1};
-    static const int32_t pref64[] = {3, 4, 2, 5, 1};
-    if (d == 128) {
-        for (int32_t g : pref128)
-            if (granules_available % g == 0) return g;
-    } else {
-        for (int32_t g : pref64)
-            if (granules_available % g == 0) return g;
-    }
-    return 1;
+// q-block size of the tile list when the caller leaves it open: the largest
+// multiple of 16 up to 64 that divides T.
+int32_t pick_bq(int32_t T) {
+    const int32_t n = T / 16;
+    for (int32_t g = 4; g >= 1; --g)
+        if (n % g == 0) return 16 * g;
+    return 16;
 }
+
+// 16-row granules per wave of the bf16 forward kernel: what two waves per
+// SIMD can hold in registers (output accumulators plus query fragments).
+int32_t kernel_granules(int32_t d) { return d == 128 ? 2 : 4; }
 
 int32_t pick_bk(int32_t T) {
     int32_t n = T / 16;
@@ -94,9 +90,7 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         return FSA_ERR_NOMEM;
     }
     try {
-        // Rows per wave of the forward kernel: 16 * granules, dividing T.
-        const int32_t granules = pick_granules(s.bq ? s.bq / 16 : s.T / 16, s.d);
-        if (s.bq == 0) s.bq = 16 * granules;
+        if (s.bq == 0) s.bq = pick_bq(s.T);
         if (s.bk == 0) s.bk = pick_bk(s.T);
         p->shape = s;
 
@@ -170,9 +164,11 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         for (int32_t f = 0; f < s.F; ++f) total += p->slice_size[f];
         p->valid_pairs = total * int64_t(s.T) * s.T;
 
-        // ---- forward geometry
+        // ---- forward geometry: each wave takes `granules` consecutive 16-row
+        // granules of one frame; a frame's last unit may hold fewer.
+        const int32_t granules = kernel_granules(s.d);
         p->forward.granules = granules;
-        p->forward.units_per_frame = s.T / (16 * granules);
+        p->forward.units_per_frame = (s.T / 16 + granules - 1) / granules;
         p->forward.groups_per_frame = (p->forward.units_per_frame + kWaves - 1) / kWaves;
         p->forward.workgroups = int64_t(s.B) * s.H * s.F * p->forward.groups_per_frame;
 

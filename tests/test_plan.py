@@ -43,7 +43,7 @@ def test_valid_pairs(F, T, w, r, bq, bk):
 
 
 @pytest.mark.parametrize("T,d,bq", [(3600, 128, 48), (8160, 128, 48), (880, 128, 16),
-                                    (48, 64, 48), (880, 64, 80), (64, 128, 32)])
+                                    (48, 64, 48), (880, 64, 16), (64, 128, 64)])
 def test_auto_block_sizes(T, d, bq):
     s = fsa.fsa_plan_shape(plan(3, T, 1, 0, 0, 0, d=d))
     assert s.bq == bq
