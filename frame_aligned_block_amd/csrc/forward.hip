@@ -264,8 +264,19 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
                                         float (&rs)[G], f32x4 (&o)[G][D / 16],
                                         const LaneAddr& la) {
     using GG = Geo<D>;
+    // The vector work of the softmax runs at raised issue priority: the other
+    // wave on this SIMD is usually in its matrix phase, and finishing the
+    // softmax quickly gets this wave back to matrix work (measured ~9%).
     if (NB == 2) {
+        bf16x8 va[GG::DB];                // V operands first: their LDS latency
+#pragma unroll                            // overlaps the softmax (measured ~6%)
+        for (int db = 0; db < GG::DB; ++db) {
+            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, la);
+            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, la);
+            va[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
         bf16x8 pk[G];
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const f32x4 sv[2] = {s[0][g], s[1][g]};
@@ -277,17 +288,15 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
             rs[g] = sum_pairs(pp, 4, rs[g]);
             pk[g] = bf16x8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-        for (int db = 0; db < GG::DB; ++db) {
-            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, la);
-            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, la);
-            const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        for (int db = 0; db < GG::DB; ++db)
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[g], o[g][db], 0, 0, 0);
-        }
+                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pk[g], o[g][db], 0, 0, 0);
     } else {
         i16x4 pk[G];
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const f32x4 sv[1] = {s[0][g]};
@@ -298,6 +307,7 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
             const bf16x4 b4 = {pp[0][0], pp[0][1], pp[1][0], pp[1][1]};
             pk[g] = __builtin_bit_cast(i16x4, b4);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) {
             const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, la));
