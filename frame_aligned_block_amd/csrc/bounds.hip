@@ -53,11 +53,13 @@ __device__ __forceinline__ PartRows part_rows(int part, int T, int rows_per_part
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
     const E* __restrict__ Q, const E* __restrict__ K, float* __restrict__ colsum,
-    float* __restrict__ qnorm, int N, int T, int rows_per_part, int ppf, int nparts) {
+    float* __restrict__ qnorm, float* __restrict__ partqmax, int N, int T, int rows_per_part,
+    int ppf, int nparts) {
     constexpr int V = Pack16<E>::n;
     constexpr int LPR = D / V;        // lanes per row
     constexpr int RPI = 256 / LPR;    // rows per iteration
     __shared__ float red[RPI][D];
+    __shared__ float qred[RPI];
 
     const int part = blockIdx.x, bh = blockIdx.y;
     const PartRows pr = part_rows(part, T, rows_per_part, ppf);
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
     float acc[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = 0.f;
+    float qbest = 0.f;
     for (int r = pr.begin + r0; r < pr.end; r += RPI) {
         const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
         const Pack16<E> q = load16(Q + base + size_t(r) * D + lane * V);
@@ -79,15 +82,23 @@ __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
         }
 #pragma unroll
         for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-        if (lane == 0) qnorm[size_t(bh) * N + r] = sqrtf(ss);
+        const float qn = sqrtf(ss);
+        qbest = fmaxf(qbest, qn);
+        if (lane == 0) qnorm[size_t(bh) * N + r] = qn;
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) red[r0][lane * V + e] = acc[e];
+    if (lane == 0) qred[r0] = qbest;
     __syncthreads();
     if (threadIdx.x < D) {
         float s = 0.f;
         for (int i = 0; i < RPI; ++i) s += red[i][threadIdx.x];
         colsum[(size_t(bh) * nparts + part) * D + threadIdx.x] = s;
+    }
+    if (threadIdx.x == D) {
+        float b = 0.f;
+        for (int i = 0; i < RPI; ++i) b = fmaxf(b, qred[i]);
+        partqmax[size_t(bh) * nparts + part] = b;
     }
 }
 
@@ -98,7 +109,9 @@ __global__ __launch_bounds__(256) void bounds_mean(const float* __restrict__ col
     const int bh = blockIdx.x, t = threadIdx.x;
     if (t >= D) return;
     float s = 0.f;
-    for (int p = 0; p < nparts; ++p) s += colsum[(size_t(bh) * nparts + p) * D + t];
+    const float* col = colsum + size_t(bh) * nparts * D + t;
+#pragma unroll 16       // loads issue ahead; the additions keep their order
+    for (int p = 0; p < nparts; ++p) s += col[size_t(p) * D];
     mu[size_t(bh) * D + t] = s / float(N);
 }
 
@@ -146,54 +159,43 @@ __global__ __launch_bounds__(256) void bounds_centre(
     }
 }
 
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    const int wave = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[wave] = v;
-    __syncthreads();
-    float r = scratch[0];
-    for (int w = 1; w < int(blockDim.x >> 6); ++w) r = fmaxf(r, scratch[w]);
-    return r;
-}
-
 // Pass 4, per (batch, head): per-frame key radius, per-slice radius, the
 // largest row bound scale * ||q_i|| * R_S(f(i)) and the eligibility flag.
+// Maxima are exact, so any reduction order gives the same bits. The largest
+// row bound of frame f is (scale * max ||q_i||) * R_S(f): rounding is monotone.
 __global__ __launch_bounds__(256) void bounds_finalize(
-    const float* __restrict__ qnorm, const float* __restrict__ partmax, float* __restrict__ rframe,
-    float* __restrict__ rslice, float* __restrict__ stat, uint8_t* __restrict__ elig, int N,
-    int T, int F, int ppf, float scale, const FrameTable tab) {
+    const float* __restrict__ partqmax, const float* __restrict__ partmax,
+    float* __restrict__ rframe, float* __restrict__ rslice, float* __restrict__ stat,
+    uint8_t* __restrict__ elig, int F, int ppf, float scale, const FrameTable tab) {
     __shared__ float rf[FSA_MAX_FRAMES + 1];
     __shared__ float qm[FSA_MAX_FRAMES + 1];
-    __shared__ float scratch[4];
+    __shared__ float sb[FSA_MAX_FRAMES + 1];
     const int bh = blockIdx.x;
     for (int g = threadIdx.x; g < F; g += blockDim.x) {
-        float b = 0.f;
-        for (int s = 0; s < ppf; ++s) b = fmaxf(b, partmax[size_t(bh) * F * ppf + g * ppf + s]);
+        float b = 0.f, q = 0.f;
+        for (int s = 0; s < ppf; ++s) {
+            b = fmaxf(b, partmax[size_t(bh) * F * ppf + g * ppf + s]);
+            q = fmaxf(q, partqmax[size_t(bh) * F * ppf + g * ppf + s]);
+        }
         rf[g] = b;
+        qm[g] = q;
         rframe[size_t(bh) * F + g] = b;
     }
-    for (int f = 0; f < F; ++f) {
-        float b = 0.f;
-        for (int i = threadIdx.x; i < T; i += blockDim.x)
-            b = fmaxf(b, qnorm[size_t(bh) * N + size_t(f) * T + i]);
-        b = block_max(b, scratch);
-        if (threadIdx.x == 0) qm[f] = b;
+    __syncthreads();
+    for (int f = threadIdx.x; f < F; f += blockDim.x) {
+        const uint32_t run = tab.runs[f];
+        const int a0 = run & 0xff, l0 = (run >> 8) & 0xff;
+        const int a1 = (run >> 16) & 0xff, l1 = run >> 24;
+        float r = 0.f;
+        for (int g = a0; g < a0 + l0; ++g) r = fmaxf(r, rf[g]);
+        for (int g = a1; g < a1 + l1; ++g) r = fmaxf(r, rf[g]);
+        rslice[size_t(bh) * F + f] = r;
+        sb[f] = (scale * qm[f]) * r;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         float st = 0.f;
-        for (int f = 0; f < F; ++f) {
-            const uint32_t run = tab.runs[f];
-            const int a0 = run & 0xff, l0 = (run >> 8) & 0xff;
-            const int a1 = (run >> 16) & 0xff, l1 = run >> 24;
-            float r = 0.f;
-            for (int g = a0; g < a0 + l0; ++g) r = fmaxf(r, rf[g]);
-            for (int g = a1; g < a1 + l1; ++g) r = fmaxf(r, rf[g]);
-            rslice[size_t(bh) * F + f] = r;
-            st = fmaxf(st, (scale * qm[f]) * r);
-        }
+        for (int f = 0; f < F; ++f) st = fmaxf(st, sb[f]);
         stat[bh] = st;
         elig[bh] = st <= FSA_ELIG_BETA ? 1 : 0;
     }
@@ -213,18 +215,18 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
     float* qn = reinterpret_cast<float*>(ws + p.ws.qnorm);
     float* colsum = reinterpret_cast<float*>(ws + p.bounds.colsum);
     float* partmax = reinterpret_cast<float*>(ws + p.bounds.partmax);
+    float* partqmax = reinterpret_cast<float*>(ws + p.bounds.partqmax);
     const dim3 grid(nparts, BH);
     hipLaunchKernelGGL((bounds_colsum_qnorm<E, D>), grid, dim3(256), 0, stream, Q, K, colsum, qn,
-                       N, s.T, p.bounds.rows_per_part, ppf, nparts);
+                       partqmax, N, s.T, p.bounds.rows_per_part, ppf, nparts);
     hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, N, nparts);
     hipLaunchKernelGGL((bounds_centre<E, D>), grid, dim3(256), 0, stream, K, mu, Kc, partmax, N,
                        s.T, p.bounds.rows_per_part, ppf, nparts);
-    hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, qn, partmax,
+    hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, partqmax, partmax,
                        reinterpret_cast<float*>(ws + p.ws.rframe),
                        reinterpret_cast<float*>(ws + p.ws.rslice),
                        reinterpret_cast<float*>(ws + p.ws.stat),
-                       reinterpret_cast<uint8_t*>(ws + p.ws.elig), N, s.T, s.F, ppf, scale,
-                       p.table);
+                       reinterpret_cast<uint8_t*>(ws + p.ws.elig), s.F, ppf, scale, p.table);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));

@@ -192,6 +192,7 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         const size_t nparts = size_t(s.F) * p->bounds.parts_per_frame;
         p->bounds.colsum = off;  off = align_up(off + BH * nparts * s.d * 4);
         p->bounds.partmax = off; off = align_up(off + BH * nparts * 4);
+        p->bounds.partqmax = off; off = align_up(off + BH * nparts * 4);
         w.total = off;
     } catch (const std::bad_alloc&) {
         delete p;
