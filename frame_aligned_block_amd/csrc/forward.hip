@@ -101,8 +101,16 @@ __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh) {
 
 // ---------------------------------------------------------------- bf16 route
 
-constexpr int kBK = 64;          // keys per LDS chunk
-constexpr int kStages = 2;       // LDS ring: chunk c+1 lands while c is consumed
+#ifndef FSA_CHUNK_KEYS
+#define FSA_CHUNK_KEYS 64
+#endif
+#ifndef FSA_STAGES
+#define FSA_STAGES 2
+#endif
+constexpr int kBK = FSA_CHUNK_KEYS;  // keys per LDS chunk (32 or 64)
+constexpr int kStages = FSA_STAGES;  // LDS ring depth: chunks c+1 .. c+kStages-1 in flight
+static_assert(kBK == 32 || kBK == 64 || kBK == 128, "chunk of 32, 64 or 128 keys");
+static_assert(kStages >= 2 && kStages <= 4, "2 to 4 stages");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -123,7 +131,9 @@ struct Geo {
     static constexpr int SUB = kBK * 64;               // one 64 x 64-byte sub-tile
     static constexpr int TILE = KS * SUB;              // one K (or V) chunk
     static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
-    static constexpr int LOADS = 2 * KS;               // wave loads (1 KB each) per chunk
+    static constexpr int RB = kBK / 16;                // 16-row blocks per sub-tile
+    static constexpr int NI = KS * RB / fsa::kWaves;   // 1 KB copies per wave per tile
+    static constexpr int LOADS = 2 * NI;               // wave copies per chunk (K and V)
 };
 
 // vmcnt(n) with no wait on the other counters (gfx9 encoding).
@@ -142,24 +152,29 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
 }
 
 // Start the asynchronous global -> LDS copy of chunk ch of the slice walk (K
-// and V straight into the stage, no registers). Wave w moves rows 16w..16w+15
-// of every sub-tile; lane l carries row 16w + l/4, 16-byte segment l%4.
+// and V straight into the stage, no registers). The tile's 1 KB blocks (16
+// rows x 64 bytes of one sub-tile) are numbered j = 4i + wave; block j is
+// sub-tile j / RB, rows 16 (j % RB) .. +15, so each wave always moves the same
+// 16 rows: lane l carries row 16 (wave % RB) + l/4, 16-byte segment l%4.
 // Positions past the slice are clamped to its last key: harmless duplicates
-// that are never read.
+// that are never read, issued anyway so every chunk has the same number of
+// copies in flight.
 template <int D>
 __device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                             const __bf16* Vh, int ch, int wave, int lane) {
     using GG = Geo<D>;
-    const int row = 16 * wave + (lane >> 2);
+    const int row = 16 * (wave % GG::RB) + (lane >> 2);
     const unsigned rowoff = unsigned(sl.key(min(ch * kBK + row, sl.total - 1))) * (2 * D);
     const int seg = lane & 3;
     const unsigned koff = rowoff + 16 * (seg ^ ((lane >> 3) & 3));     // (row >> 1) & 3
     const unsigned voff = rowoff + 16 * (seg ^ (((lane >> 4) & 1) << 1));
 #pragma unroll
-    for (int i = 0; i < GG::KS; ++i) {
-        const unsigned dst = stage_lds + i * GG::SUB + wave * 1024;
-        lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * i, koff);
-        lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * i, voff);
+    for (int i = 0; i < GG::NI; ++i) {
+        const int j = i * fsa::kWaves + wave;
+        const int t = j / GG::RB;                      // sub-tile = 32-column block
+        const unsigned dst = stage_lds + t * GG::SUB + (j % GG::RB) * 1024;
+        lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * t, koff);
+        lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * t, voff);
     }
 }
 
@@ -318,12 +333,12 @@ __device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const
     }
 }
 
-// The slice walk of one workgroup. Chunks of 64 keys stream into a 2-stage
-// LDS ring by direct-to-LDS loads issued one chunk ahead; each chunk is
-// waited for (vmcnt) and published by one barrier. Per 32-key step a wave
-// computes S^T, its softmax and P.V in sequence; two workgroups share each CU
-// (two waves per SIMD), so one wave's matrix work overlaps the other's vector
-// work in hardware.
+// The slice walk of one workgroup. Chunks of kBK keys stream into a
+// kStages-deep LDS ring by direct-to-LDS copies issued kStages-1 chunks ahead;
+// a chunk is waited for (vmcnt) once the chunk before it is consumed and is
+// published by one barrier. Per 32-key step a wave computes S^T, its softmax
+// and P.V in sequence; two workgroups share each CU (two waves per SIMD), so
+// one wave's matrix work overlaps the other's vector work in hardware.
 template <int D, int G, bool FIXED>
 __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
@@ -337,40 +352,49 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
 
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
-    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
-    FSA_WAIT_VMCNT(0);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+        issue_chunk<D>(smem_lds + i * GG::STAGE, sl, Kh, Vh, i, wave, lane);
+    FSA_WAIT_VMCNT((kStages - 2) * GG::LOADS);          // chunk 0 has landed
     __builtin_amdgcn_s_barrier();
 
     f32x4 sv[2][G];
+    int st = 0;                                         // stage of chunk ch
     for (int ch = 0; ch < nchunks; ++ch) {
-        const unsigned char* S0 = smem + (ch & 1) * GG::STAGE;
-        if (ch + 1 < nchunks)
-            issue_chunk<D>(smem_lds + ((ch + 1) & 1) * GG::STAGE, sl, Kh, Vh, ch + 1, wave, lane);
-        const int left = sl.total - ch * kBK;        // keys left, a multiple of 16
+        const unsigned char* S0 = smem + st * GG::STAGE;
+        const int st_next = st == kStages - 1 ? 0 : st + 1;
+        const int st_fill = st == 0 ? kStages - 1 : st - 1;   // held chunk ch-1
+        issue_chunk<D>(smem_lds + st_fill * GG::STAGE, sl, Kh, Vh, ch + kStages - 1, wave, lane);
+        const int left = sl.total - ch * kBK;            // keys left, a multiple of 16
         if (left >= kBK) {
-            scores<D, G, 2>(S0, 0, qf, sv, la);
-            pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sv, c, shift, m, rs, o, la);
-            scores<D, G, 2>(S0, 32, qf, sv, la);
-            pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 32, sv, c, shift, m, rs, o, la);
-        } else {                                     // the final chunk: 16, 32 or 48 keys
-            if (left >= 32) {
-                scores<D, G, 2>(S0, 0, qf, sv, la);
-                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, 0, sv, c, shift, m, rs, o, la);
+#pragma unroll
+            for (int k0 = 0; k0 < kBK; k0 += 32) {
+                scores<D, G, 2>(S0, k0, qf, sv, la);
+                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, k0, sv, c, shift, m, rs, o, la);
+            }
+        } else {                                         // the final chunk: whole granules
+            for (int k0 = 0; k0 + 32 <= left; k0 += 32) {
+                scores<D, G, 2>(S0, k0, qf, sv, la);
+                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, k0, sv, c, shift, m, rs, o, la);
             }
             if (left & 16) {
-                const int koff = left & 32;
+                const int koff = left - 16;
                 scores<D, G, 1>(S0, koff, qf, sv, la);
                 pv_step<D, G, FIXED, 1>(S0 + GG::TILE, koff, sv, c, shift, m, rs, o, la);
             }
         }
-        FSA_WAIT_VMCNT(0);                           // chunk ch+1 has landed
+        FSA_WAIT_VMCNT((kStages - 2) * GG::LOADS);      // chunk ch+1 has landed
         __builtin_amdgcn_s_barrier();
+        st = st_next;
     }
+    FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
 }
 
-// Workgroups per CU: two (two waves per SIMD, <= 256 registers per lane)
-// while a wave's accumulators and query fragments fit, else one.
-constexpr int fwd_occupancy(int D, int G) { return G * D <= 256 ? 2 : 1; }
+// Workgroups per CU for two waves per SIMD (<= 256 registers per lane) while
+// a wave's accumulators and query fragments fit, else one wave per SIMD.
+constexpr int fwd_occupancy(int D, int G) {
+    return G * D <= 256 ? (2 * 4 / fsa::kWaves > 0 ? 2 * 4 / fsa::kWaves : 1) : 1;
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {

@@ -25,7 +25,10 @@ struct FrameTable {
 
 // Query rows per wave = 16 * granules; a workgroup holds kWaves waves of
 // consecutive row units of one frame.
-constexpr int kWaves = 4;
+#ifndef FSA_WAVES
+#define FSA_WAVES 4
+#endif
+constexpr int kWaves = FSA_WAVES;
 constexpr int kThreads = 64 * kWaves;
 
 struct BoundsGeometry {
