@@ -104,13 +104,8 @@ __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh) {
 #ifndef FSA_CHUNK_KEYS
 #define FSA_CHUNK_KEYS 64
 #endif
-#ifndef FSA_STAGES
-#define FSA_STAGES 2
-#endif
-constexpr int kBK = FSA_CHUNK_KEYS;  // keys per LDS chunk (32 or 64)
-constexpr int kStages = FSA_STAGES;  // LDS ring depth: chunks c+1 .. c+kStages-1 in flight
+constexpr int kBK = FSA_CHUNK_KEYS;  // keys per LDS chunk; two chunks in LDS
 static_assert(kBK == 32 || kBK == 64 || kBK == 128, "chunk of 32, 64 or 128 keys");
-static_assert(kStages >= 2 && kStages <= 4, "2 to 4 stages");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -270,81 +265,145 @@ __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const flo
     }
 }
 
-// Softmax and O^T += V^T P^T for the 32 keys at koff (NB = 2) or the lone
-// 16-key granule at koff (NB = 1, K = 16 products). The row sum adds the
-// bf16-rounded probabilities, the same values the product consumes.
+// V^T operands of the 32 keys at koff for all D/16 column blocks: the two
+// 16-key halves form the two k-groups of the 16x16x32 B operand.
+template <int D>
+__device__ __forceinline__ void load_v(const unsigned char* Vs, int koff, bf16x8 (&va)[D / 16],
+                                       const LaneAddr& la) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, la);
+        const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, la);
+        va[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+}
+
+// Softmax of one 32-key step (NB = 2) or of the lone 16-key granule (NB = 1)
+// into packed bf16 probabilities, the B operand of O^T += V^T P^T. The row
+// sum adds the bf16-rounded probabilities, the values the product consumes.
 template <int D, int G, bool FIXED, int NB>
-__device__ __forceinline__ void pv_step(const unsigned char* Vs, int koff, const f32x4 (&s)[2][G],
-                                        float c, const float (&shift)[G], float (&m)[G],
-                                        float (&rs)[G], f32x4 (&o)[G][D / 16],
-                                        const LaneAddr& la) {
+__device__ __forceinline__ void softmax(const f32x4 (&s)[2][G], float c, const float (&shift)[G],
+                                        float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
+                                        bf16x2 (&pk)[G][2 * NB]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const f32x4 sv[2] = {s[0][g], s[1][g]};
+        float p[4 * NB];
+        probs<D, G, FIXED, 4 * NB>(sv, g, c, shift, m, rs, o, p);
+#pragma unroll
+        for (int i = 0; i < 2 * NB; ++i) pk[g][i] = bf16x2{__bf16(p[2 * i]), __bf16(p[2 * i + 1])};
+        rs[g] = sum_pairs(pk[g], 2 * NB, rs[g]);
+    }
+}
+
+// K operands of the 32 keys at koff: 16 rows per 16-key block, all D/32
+// k-steps of the S^T product.
+template <int D>
+__device__ __forceinline__ void load_k(const unsigned char* Ks, int koff, bf16x8 (&ka)[D / 32][2],
+                                       const LaneAddr& la) {
     using GG = Geo<D>;
-    // The vector work of the softmax runs at raised issue priority: the other
-    // wave on this SIMD is usually in its matrix phase, and finishing the
-    // softmax quickly gets this wave back to matrix work (measured ~9%).
-    if (NB == 2) {
-        bf16x8 va[GG::DB];                // V operands first: their LDS latency
-#pragma unroll                            // overlaps the softmax (measured ~6%)
-        for (int db = 0; db < GG::DB; ++db) {
-            const bf16x4 v0 = v_operand<D>(Vs, koff, 0, db, la);
-            const bf16x4 v1 = v_operand<D>(Vs, koff, 1, db, la);
-            va[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        }
-        bf16x8 pk[G];
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const f32x4 sv[2] = {s[0][g], s[1][g]};
-            float p[8];
-            probs<D, G, FIXED, 8>(sv, g, c, shift, m, rs, o, p);
-            bf16x2 pp[4];
+    for (int ks = 0; ks < GG::KS; ++ks)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pp[i] = bf16x2{__bf16(p[2 * i]), __bf16(p[2 * i + 1])};
-            rs[g] = sum_pairs(pp, 4, rs[g]);
-            pk[g] = bf16x8{pp[0][0], pp[0][1], pp[1][0], pp[1][1], pp[2][0], pp[2][1], pp[3][0], pp[3][1]};
-        }
-        __builtin_amdgcn_s_setprio(0);
+        for (int b = 0; b < 2; ++b)
+            ka[ks][b] = *reinterpret_cast<const bf16x8*>(Ks + ks * GG::SUB + (koff + 16 * b) * 64 + la.k);
+}
+
+template <int G>
+__device__ __forceinline__ bf16x8 pack_p(const bf16x2 (&pk)[G][4], int g) {
+    return bf16x8{pk[g][0][0], pk[g][0][1], pk[g][1][0], pk[g][1][1],
+                  pk[g][2][0], pk[g][2][1], pk[g][3][0], pk[g][3][1]};
+}
+
+// The matrix phase of a step: S^T of the next 32 keys (sn, from their K
+// operands ka) and O^T += V^T P^T of this step, issued interleaved so that
+// consecutive products never share an accumulator (the S^T products form
+// only 2G dependent chains of D/32 links each).
+template <int D, int G>
+__device__ __forceinline__ void qk_pv(const bf16x8 (&ka)[D / 32][2], const bf16x8 (&qf)[G][D / 32],
+                                      f32x4 (&sn)[2][G], const bf16x8 (&va)[D / 16],
+                                      const bf16x2 (&pk)[G][4], f32x4 (&o)[G][D / 16]) {
+    using GG = Geo<D>;
+    constexpr int DPK = GG::DB / GG::KS;                // P.V column blocks per k-step
 #pragma unroll
-        for (int db = 0; db < GG::DB; ++db)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pk[g], o[g][db], 0, 0, 0);
-    } else {
-        i16x4 pk[G];
-        __builtin_amdgcn_s_setprio(1);
+        for (int g = 0; g < G; ++g) sn[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const f32x4 sv[1] = {s[0][g]};
-            float p[4];
-            probs<D, G, FIXED, 4>(sv, g, c, shift, m, rs, o, p);
-            bf16x2 pp[2] = {bf16x2{__bf16(p[0]), __bf16(p[1])}, bf16x2{__bf16(p[2]), __bf16(p[3])}};
-            rs[g] = sum_pairs(pp, 2, rs[g]);
-            const bf16x4 b4 = {pp[0][0], pp[0][1], pp[1][0], pp[1][1]};
-            pk[g] = __builtin_bit_cast(i16x4, b4);
-        }
-        __builtin_amdgcn_s_setprio(0);
+    for (int ks = 0; ks < GG::KS; ++ks) {
 #pragma unroll
-        for (int db = 0; db < GG::DB; ++db) {
-            const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, la));
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[g], o[g][db], 0, 0, 0);
+                sn[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks][b], qf[g][ks], sn[b][g], 0, 0, 0);
+#pragma unroll
+        for (int db = ks * DPK; db < (ks + 1) * DPK; ++db)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pack_p<G>(pk, g), o[g][db], 0, 0, 0);
+    }
+}
+
+// O^T += V^T P^T for one 32-key step (the last step: no next scores).
+template <int D, int G>
+__device__ __forceinline__ void pv(const bf16x8 (&va)[D / 16], const bf16x2 (&pk)[G][4],
+                                   f32x4 (&o)[G][D / 16]) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pack_p<G>(pk, g), o[g][db], 0, 0, 0);
+}
+
+// O^T += V^T P^T for the lone 16-key granule at koff (K = 16 products).
+template <int D, int G>
+__device__ __forceinline__ void pv_half(const unsigned char* Vs, int koff, const bf16x2 (&pk)[G][2],
+                                        f32x4 (&o)[G][D / 16], const LaneAddr& la) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const i16x4 va = __builtin_bit_cast(i16x4, v_operand<D>(Vs, koff, 0, db, la));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const bf16x4 b = {pk[g][0][0], pk[g][0][1], pk[g][1][0], pk[g][1][1]};
+            o[g][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, __builtin_bit_cast(i16x4, b),
+                                                                 o[g][db], 0, 0, 0);
         }
     }
 }
 
-// The slice walk of one workgroup. Chunks of kBK keys stream into a
-// kStages-deep LDS ring by direct-to-LDS copies issued kStages-1 chunks ahead;
-// a chunk is waited for (vmcnt) once the chunk before it is consumed and is
-// published by one barrier. Per 32-key step a wave computes S^T, its softmax
-// and P.V in sequence; two workgroups share each CU (two waves per SIMD), so
-// one wave's matrix work overlaps the other's vector work in hardware.
+// lgkmcnt(0) with no wait on the other counters (gfx9 encoding).
+#define FSA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
+
+#ifndef FSA_PRIO
+#define FSA_PRIO 1
+#endif
+// Issue priority of the vector phase (FSA_PRIO 1) or of the matrix phase (2).
+__device__ __forceinline__ void prio_vector_begin() { if (FSA_PRIO == 1) __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_vector_end() { if (FSA_PRIO == 1) __builtin_amdgcn_s_setprio(0); }
+__device__ __forceinline__ void prio_matrix_begin() { if (FSA_PRIO == 2) __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_matrix_end() { if (FSA_PRIO == 2) __builtin_amdgcn_s_setprio(0); }
+
+// The slice walk of one workgroup. Each 32-key step t runs in two phases: a
+// vector phase (the softmax of S_t, while this step's V operands and the next
+// step's K operands load from LDS) and a matrix phase (S_{t+1} and P_t V_t,
+// interleaved). Two waves share each SIMD (two workgroups per CU); one wave's
+// vector phase overlaps the other's matrix phase, which the hardware does far
+// better than mixing the two kinds of work within one wave.
+// Chunks of kBK keys stream into a two-stage LDS ring by direct-to-LDS
+// copies issued one chunk ahead. At the last step of a chunk the wave holds
+// that step's V operands in registers, waits for the next chunk's copies and
+// passes one barrier: no wave reads the old stage after it, so the copy of
+// the chunk after next goes there. Every chunk but the last is full; the
+// last holds 16 to kBK keys, whole 16-key granules. Scores are always
+// computed for 32 keys: past the slice end a stage holds copies of the
+// slice's last key (finite values) whose scores are never used.
 template <int D, int G, bool FIXED>
 __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
                                        const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
                                        float (&rs)[G], int wave, int lane) {
     using GG = Geo<D>;
+    constexpr int SPC = kBK / 32;                       // 32-key steps per chunk
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
     const int nchunks = (sl.total + kBK - 1) / kBK;
     float m[G];
@@ -352,40 +411,66 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
 
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-        issue_chunk<D>(smem_lds + i * GG::STAGE, sl, Kh, Vh, i, wave, lane);
-    FSA_WAIT_VMCNT((kStages - 2) * GG::LOADS);          // chunk 0 has landed
+    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    FSA_WAIT_VMCNT(0);                                  // chunk 0 has landed
     __builtin_amdgcn_s_barrier();
+    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
 
     f32x4 sv[2][G];
+    scores<D, G, 2>(smem, 0, qf, sv, la);
     int st = 0;                                         // stage of chunk ch
-    for (int ch = 0; ch < nchunks; ++ch) {
+    for (int ch = 0; ch + 1 < nchunks; ++ch) {
         const unsigned char* S0 = smem + st * GG::STAGE;
-        const int st_next = st == kStages - 1 ? 0 : st + 1;
-        const int st_fill = st == 0 ? kStages - 1 : st - 1;   // held chunk ch-1
-        issue_chunk<D>(smem_lds + st_fill * GG::STAGE, sl, Kh, Vh, ch + kStages - 1, wave, lane);
-        const int left = sl.total - ch * kBK;            // keys left, a multiple of 16
-        if (left >= kBK) {
 #pragma unroll
-            for (int k0 = 0; k0 < kBK; k0 += 32) {
-                scores<D, G, 2>(S0, k0, qf, sv, la);
-                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, k0, sv, c, shift, m, rs, o, la);
+        for (int s = 0; s < SPC; ++s) {
+            bf16x8 va[GG::DB];
+            load_v<D>(S0 + GG::TILE, 32 * s, va, la);
+            bf16x8 ka[GG::KS][2];
+            if (s + 1 < SPC) {
+                load_k<D>(S0, 32 * (s + 1), ka, la);
+            } else {
+                FSA_WAIT_VMCNT(0);                      // chunk ch+1 has landed
+                FSA_WAIT_LGKM0();                       // this step's V is in registers
+                __builtin_amdgcn_s_barrier();
+                if (ch + 2 < nchunks)
+                    issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+                st ^= 1;
+                load_k<D>(smem + st * GG::STAGE, 0, ka, la);
             }
-        } else {                                         // the final chunk: whole granules
-            for (int k0 = 0; k0 + 32 <= left; k0 += 32) {
-                scores<D, G, 2>(S0, k0, qf, sv, la);
-                pv_step<D, G, FIXED, 2>(S0 + GG::TILE, k0, sv, c, shift, m, rs, o, la);
-            }
-            if (left & 16) {
-                const int koff = left - 16;
-                scores<D, G, 1>(S0, koff, qf, sv, la);
-                pv_step<D, G, FIXED, 1>(S0 + GG::TILE, koff, sv, c, shift, m, rs, o, la);
-            }
+            bf16x2 pk[G][4];
+            prio_vector_begin();
+            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            prio_vector_end();
+            __builtin_amdgcn_sched_barrier(0);
+            prio_matrix_begin();
+            qk_pv<D, G>(ka, qf, sv, va, pk, o);
+            prio_matrix_end();
+            __builtin_amdgcn_sched_barrier(0);
         }
-        FSA_WAIT_VMCNT((kStages - 2) * GG::LOADS);      // chunk ch+1 has landed
-        __builtin_amdgcn_s_barrier();
-        st = st_next;
+    }
+
+    // The last chunk; sv holds the scores of its first step.
+    const unsigned char* S0 = smem + st * GG::STAGE;
+    const int left = sl.total - (nchunks - 1) * kBK;    // 16 .. kBK keys
+    int k0 = 0;
+    for (; k0 + 32 <= left; k0 += 32) {
+        bf16x8 va[GG::DB];
+        load_v<D>(S0 + GG::TILE, k0, va, la);
+        bf16x2 pk[G][4];
+        if (k0 + 32 < left) {
+            bf16x8 ka[GG::KS][2];
+            load_k<D>(S0, k0 + 32, ka, la);
+            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            qk_pv<D, G>(ka, qf, sv, va, pk, o);
+        } else {
+            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            pv<D, G>(va, pk, o);
+        }
+    }
+    if (left & 16) {                                    // the lone granule at k0
+        bf16x2 pk[G][2];
+        softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+        pv_half<D, G>(S0 + GG::TILE, k0, pk, o, la);
     }
     FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
 }
@@ -399,7 +484,7 @@ constexpr int fwd_occupancy(int D, int G) {
 template <int D, int G>
 __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {
     using GG = Geo<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * GG::STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * GG::STAGE];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
