@@ -23,10 +23,12 @@ forward launch inside the timed loop.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -106,6 +108,19 @@ def cpu_baseline(cfg, Q, K, V, seconds: float):
                       f"{spent:.1f} s; fp64 numpy, BLAS on {threads} threads"}
 
 
+def current_sclk_mhz():
+    """The GPU's current shader clock from the amdgpu sysfs table (the line
+    marked '*'), read right after the timed region; None where unavailable."""
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for ln in open(path).read().splitlines():
+                if ln.rstrip().endswith("*"):
+                    return int(ln.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
 def calibrate_copy(nbytes: int) -> None:
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -182,8 +197,11 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    bnd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    bnd = [e[0].elapsed_time(e[1]) for e in ev]
+    fwd = [e[1].elapsed_time(e[2]) for e in ev]
+    bnd_ms = sum(bnd) / args.steps
+    fwd_ms = sum(fwd) / args.steps
+    sclk = current_sclk_mhz()
 
     # A/B: the same forward with every head on the online path
     ab = None
@@ -202,7 +220,7 @@ def main() -> int:
               "online_only_forward_tflops": round(flops / on_ms / 1e9, 2),
               "fixed_max_speedup": round(on_ms / fwd_ms, 4)}
 
-    elig = fsa.workspace_views(plan, ws)["elig"].float().mean().item()
+    elig = float(fsa.fsa_copy_eligibility(plan, ws, stream).mean())
     bf16 = cfg.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     achieved = flops / fwd_ms / 1e9
@@ -228,7 +246,10 @@ def main() -> int:
         "ms_per_call": round(ms_step, 4),
         "pct_bf16_peak": round(100.0 * flops / ms_step / 1e9 / PEAK_BF16_TFLOPS, 2),
         "forward_ms": round(fwd_ms, 4),
+        "forward_ms_median": round(statistics.median(fwd), 4),
         "bounds_ms": round(bnd_ms, 4),
+        "bounds_ms_median": round(statistics.median(bnd), 4),
+        "sclk_mhz_after_timing": sclk,
         "eligible_head_fraction": round(elig, 4),
         "ab": ab,
         "roofline": {"kernel": "fwd_bf16" if bf16 else "fwd_f32",

@@ -114,6 +114,27 @@ extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const voi
     return fsa::launch_forward(*plan, Q, K, V, O, ws, scale, mode, stream);
 }
 
+extern "C" fsa_status fsa_copy_eligibility(const fsa_plan* plan, const void* ws,
+                                           uint8_t* host_out, hipStream_t stream) {
+    if (!plan || !host_out) {
+        set_error("fsa_copy_eligibility: NULL plan or host_out");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!ws || !aligned(ws, 256)) {
+        set_error("fsa_copy_eligibility: workspace missing or not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    const size_t n = size_t(plan->shape.B) * plan->shape.H;
+    hipError_t err = hipMemcpyAsync(host_out, static_cast<const char*>(ws) + plan->ws.elig, n,
+                                    hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) {
+        set_error("fsa_copy_eligibility: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return FSA_OK;
+}
+
 namespace {
 
 using Key = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t>;

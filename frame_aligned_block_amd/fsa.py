@@ -43,7 +43,8 @@ FSA_MAX_FRAMES = 255
 EXPORTS = (
     "fsa_plan_create", "fsa_plan_destroy", "fsa_plan_shape", "fsa_plan_export",
     "fsa_plan_valid_pairs", "fsa_workspace_bytes", "fsa_workspace_layout",
-    "fsa_bounds", "fsa_forward", "fsa_attention", "fsa_attention_workspace_bytes",
+    "fsa_bounds", "fsa_forward", "fsa_copy_eligibility", "fsa_attention",
+    "fsa_attention_workspace_bytes",
     "fsa_cache_clear", "fsa_status_string", "fsa_last_error",
 )
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.fsa_bounds.restype = c_int32
     L.fsa_forward.argtypes = [P, P, P, P, P, P, c_float, c_int32, P]
     L.fsa_forward.restype = c_int32
+    L.fsa_copy_eligibility.argtypes = [P, P, P, P]
+    L.fsa_copy_eligibility.restype = c_int32
     L.fsa_attention.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_float,
                                 c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]
     L.fsa_attention.restype = c_int32
@@ -229,6 +232,15 @@ def fsa_forward(plan: Plan, Q, K, V, O, ws, scale: float, mode=FSA_MODE_AUTO,
     mode = MODES[mode] if isinstance(mode, str) else int(mode)
     _check(lib().fsa_forward(plan, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(ws), float(scale),
                              mode, _stream(stream)))
+
+
+def fsa_copy_eligibility(plan: Plan, ws, stream=None):
+    """The B*H eligibility flags fsa_bounds wrote into ws, as a uint8 numpy
+    array of shape (B, H); synchronizes the stream."""
+    shape = fsa_plan_shape(plan)
+    out = np.zeros((shape.B, shape.H), dtype=np.uint8)
+    _check(lib().fsa_copy_eligibility(plan, _ptr(ws), out.ctypes.data, _stream(stream)))
+    return out
 
 
 def fsa_attention(Q, K, V, O, F, T, window, ref_frame, scale, B, H, d, dtype, mode, ws,

@@ -175,6 +175,21 @@ fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const void* K, const
                        void* O, const void* ws, float scale, int32_t mode, hipStream_t stream);
 
 /*
+ * fsa_copy_eligibility -- copy the B*H eligibility flags (uint8, 1 = the head
+ * takes the fixed-max route under AUTO; index b*H + h) that fsa_bounds wrote
+ * into ws, to host memory at host_out (caller-owned, at least B*H bytes). The
+ * copy is ordered on `stream` after the work already queued there, and the
+ * call returns once the flags are on the host (it synchronizes the stream).
+ * The flag is the per-head check of "Unchaining the Softmax" ¶3: the head's
+ * largest row bound is at most FSA_ELIG_BETA.
+ * Errors: FSA_ERR_INVALID_ARG (NULL plan or host_out), FSA_ERR_WORKSPACE (ws
+ * NULL or not 256-byte aligned), FSA_ERR_HIP (copy or synchronization failed,
+ * including a fault of earlier work on the stream).
+ */
+fsa_status fsa_copy_eligibility(const fsa_plan* plan, const void* ws, uint8_t* host_out,
+                                hipStream_t stream);
+
+/*
  * fsa_attention -- fsa_bounds then fsa_forward with a plan built for the
  * given shape and cached per shape (bq = bk = 0, the cache is guarded by a
  * mutex; this is the only call that allocates, host memory, on a cache miss).

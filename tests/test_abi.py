@@ -81,6 +81,12 @@ def test_bounds_and_forward_validate_before_launch():
          fsa.FSA_ERR_INVALID_ARG),
         (lambda: fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE * 64, FAKE * 128, FAKE * 128, 0.125, 0, 0),
          fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_copy_eligibility(p, None, 0), fsa.FSA_ERR_WORKSPACE),
+        (lambda: fsa.fsa_copy_eligibility(p, FAKE + 16, 0), fsa.FSA_ERR_WORKSPACE),
+        (lambda: fsa._check(fsa.lib().fsa_copy_eligibility(p, FAKE, None, None)),
+         fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa._check(fsa.lib().fsa_copy_eligibility(None, FAKE, FAKE, None)),
+         fsa.FSA_ERR_INVALID_ARG),
     ]
     for call, status in cases:
         with pytest.raises(fsa.FsaError) as e:

@@ -70,6 +70,9 @@ def test_bounds_parity_stress_heads():
     elig = run.views()["elig"][0].cpu().numpy()
     want = np.array([0 if cfg.is_loose(h) else 1 for h in range(cfg.H)])
     assert np.array_equal(elig, want)
+    # the same flags through the C ABI's host copy
+    host = fsa.fsa_copy_eligibility(run.plan, run.ws)
+    assert host.shape == (1, cfg.H) and np.array_equal(host[0], want)
 
 
 def test_k_is_not_written():
