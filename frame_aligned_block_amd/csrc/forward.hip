@@ -475,6 +475,30 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
     FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
 }
 
+// A wave that owns no query rows (past the last unit of its frame) still
+// moves its share of every chunk and passes the same barriers as the waves
+// that compute, in the same order, but issues no matrix or softmax work.
+template <int D>
+__device__ __forceinline__ void copy_only(unsigned char* smem, const Slice& sl, const __bf16* Kh,
+                                          const __bf16* Vh, int wave, int lane) {
+    using GG = Geo<D>;
+    const int nchunks = (sl.total + kBK - 1) / kBK;
+    const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
+    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    FSA_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
+    int st = 0;
+    for (int ch = 0; ch + 1 < nchunks; ++ch) {
+        FSA_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        if (ch + 2 < nchunks)
+            issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+        st ^= 1;
+    }
+    FSA_WAIT_VMCNT(0);
+}
+
 // Workgroups per CU for two waves per SIMD (<= 256 registers per lane) while
 // a wave's accumulators and query fragments fit, else one wave per SIMD.
 constexpr int fwd_occupancy(int D, int G) {
@@ -505,12 +529,18 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
 
     // A wave owns granules unit*G .. unit*G+G-1 of frame f. Granules past the
-    // frame (the tail of a frame whose granule count G does not divide, or a
-    // whole wave past the last unit) repeat the frame's last granule and are
-    // not stored: every wave runs the same loop, with no predicate inside it.
+    // frame (the tail of a frame whose granule count G does not divide)
+    // repeat the frame's last granule and are not stored: every computing
+    // wave runs the same loop, with no predicate inside it. A wave wholly
+    // past the last unit only helps stage the keys.
     const int unit = gq * fsa::kWaves + wave;
     const int ngran = T >> 4;
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    if (__builtin_amdgcn_readfirstlane(nvalid) == 0) {
+        copy_only<D>(smem, sl, Kh, Vh, uwave, lane);
+        return;
+    }
     const float c = p.c;
 
     bf16x8 qf[G][GG::KS];
@@ -529,7 +559,6 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
         for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int uwave = __builtin_amdgcn_readfirstlane(wave);
     if (fixed)
         attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
     else
