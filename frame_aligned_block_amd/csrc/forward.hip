@@ -154,23 +154,28 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
 // Positions past the slice are clamped to its last key: harmless duplicates
 // that are never read, issued anyway so every chunk has the same number of
 // copies in flight.
+// Block group i (0 <= i < NI) of a chunk's copies: one K and one V copy.
 template <int D>
-__device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
-                                            const __bf16* Vh, int ch, int wave, int lane) {
+__device__ __forceinline__ void issue_group(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
+                                            const __bf16* Vh, int ch, int wave, int lane, int i) {
     using GG = Geo<D>;
     const int row = 16 * (wave % GG::RB) + (lane >> 2);
     const unsigned rowoff = unsigned(sl.key(min(ch * kBK + row, sl.total - 1))) * (2 * D);
     const int seg = lane & 3;
     const unsigned koff = rowoff + 16 * (seg ^ ((lane >> 3) & 3));     // (row >> 1) & 3
     const unsigned voff = rowoff + 16 * (seg ^ (((lane >> 4) & 1) << 1));
+    const int j = i * fsa::kWaves + wave;
+    const int t = j / GG::RB;                          // sub-tile = 32-column block
+    const unsigned dst = stage_lds + t * GG::SUB + (j % GG::RB) * 1024;
+    lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * t, koff);
+    lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * t, voff);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
+                                            const __bf16* Vh, int ch, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < GG::NI; ++i) {
-        const int j = i * fsa::kWaves + wave;
-        const int t = j / GG::RB;                      // sub-tile = 32-column block
-        const unsigned dst = stage_lds + t * GG::SUB + (j % GG::RB) * 1024;
-        lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * t, koff);
-        lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * t, voff);
-    }
+    for (int i = 0; i < Geo<D>::NI; ++i) issue_group<D>(stage_lds, sl, Kh, Vh, ch, wave, lane, i);
 }
 
 // Per-lane LDS byte offsets (constant for the whole walk).
@@ -319,10 +324,15 @@ __device__ __forceinline__ bf16x8 pack_p(const bf16x2 (&pk)[G][4], int g) {
 // operands ka) and O^T += V^T P^T of this step, issued interleaved so that
 // consecutive products never share an accumulator (the S^T products form
 // only 2G dependent chains of D/32 links each).
-template <int D, int G>
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int D, int G, typename Hook = NoHook>
 __device__ __forceinline__ void qk_pv(const bf16x8 (&ka)[D / 32][2], const bf16x8 (&qf)[G][D / 32],
                                       f32x4 (&sn)[2][G], const bf16x8 (&va)[D / 16],
-                                      const bf16x2 (&pk)[G][4], f32x4 (&o)[G][D / 16]) {
+                                      const bf16x2 (&pk)[G][4], f32x4 (&o)[G][D / 16],
+                                      const Hook& hook = Hook()) {
     using GG = Geo<D>;
     constexpr int DPK = GG::DB / GG::KS;                // P.V column blocks per k-step
 #pragma unroll
@@ -341,6 +351,7 @@ __device__ __forceinline__ void qk_pv(const bf16x8 (&ka)[D / 32][2], const bf16x
 #pragma unroll
             for (int g = 0; g < G; ++g)
                 o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pack_p<G>(pk, g), o[g][db], 0, 0, 0);
+        hook(ks);                                       // work issued between k-steps
     }
 }
 
@@ -432,7 +443,7 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
                 FSA_WAIT_VMCNT(0);                      // chunk ch+1 has landed
                 FSA_WAIT_LGKM0();                       // this step's V is in registers
                 __builtin_amdgcn_s_barrier();
-                if (ch + 2 < nchunks)
+                if (FIXED && ch + 2 < nchunks)
                     issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
                 st ^= 1;
                 load_k<D>(smem + st * GG::STAGE, 0, ka, la);
@@ -443,7 +454,20 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
             prio_vector_end();
             __builtin_amdgcn_sched_barrier(0);
             prio_matrix_begin();
-            qk_pv<D, G>(ka, qf, sv, va, pk, o);
+            if (!FIXED && s + 1 == SPC) {
+                // Online route: the copies of the chunk after next are issued
+                // between the k-steps of the matrix phase, which measured faster
+                // for it than issuing them right after the barrier (the fixed
+                // route is faster the other way). Past the last chunk they
+                // repeat the slice's last key into the free stage, never read.
+                const unsigned dst = smem_lds + (st ^ 1) * GG::STAGE;
+                static_assert(GG::NI <= GG::KS, "one copy group per k-step");
+                qk_pv<D, G>(ka, qf, sv, va, pk, o, [&](int ks) {
+                    if (ks < GG::NI) issue_group<D>(dst, sl, Kh, Vh, ch + 2, wave, lane, ks);
+                });
+            } else {
+                qk_pv<D, G>(ka, qf, sv, va, pk, o);
+            }
             prio_matrix_end();
             __builtin_amdgcn_sched_barrier(0);
         }
