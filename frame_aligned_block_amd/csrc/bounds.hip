@@ -1,4 +1,4 @@
-// Bounds kernels: key mean, centred keys, norms and per-head eligibility.
+// Bounds kernels: key mean, centred key radii, norms and per-head eligibility.
 //
 // Source: "HeyGen 与 Google Cloud：将 Avatar IV 部署到 TPU"
 // (news.xcc.im/article/5328), "Unchaining the Softmax" ¶2-¶3. By
@@ -8,8 +8,11 @@
 // taken over the row's own slice; heads whose bound is too loose are flagged
 // for the online route.
 //
-// HBM-bound: K is read twice (mean, then centring), Q once, Kc written once.
-// Every reduction is deterministic: sums in a fixed order, maxima exact.
+// HBM-bound: K is read twice (mean, then the radii of the centred keys) and Q
+// once; nothing of the size of K is written. The centred keys themselves are
+// never stored: the forward pass scores K as given and moves each row's shift
+// by scale * q.mu instead. Every reduction is deterministic: sums in a fixed
+// order, maxima exact.
 #include <hip/hip_runtime.h>
 
 #include "fsa_internal.h"
@@ -115,12 +118,11 @@ __global__ __launch_bounds__(256) void bounds_mean(const float* __restrict__ col
     mu[size_t(bh) * D + t] = s / float(N);
 }
 
-// Pass 3: Kc = round(K - mu) to E, and the part's largest ||Kc_j|| computed
-// from the rounded values the forward kernel will consume.
+// Pass 3: the part's largest ||k_j - mu||, in fp32 from the keys as given.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void bounds_centre(
-    const E* __restrict__ K, const float* __restrict__ mu, E* __restrict__ Kc,
-    float* __restrict__ partmax, int N, int T, int rows_per_part, int ppf, int nparts) {
+__global__ __launch_bounds__(256) void bounds_radius(
+    const E* __restrict__ K, const float* __restrict__ mu, float* __restrict__ partmax, int N,
+    int T, int rows_per_part, int ppf, int nparts) {
     constexpr int V = Pack16<E>::n;
     constexpr int LPR = D / V;
     constexpr int RPI = 256 / LPR;
@@ -137,15 +139,12 @@ __global__ __launch_bounds__(256) void bounds_centre(
     float best = 0.f;
     for (int r = pr.begin + r0; r < pr.end; r += RPI) {
         const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
-        Pack16<E> c;
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            c.v[e] = E(float(k.v[e]) - m[e]);
-            const float ce = float(c.v[e]);
+            const float ce = float(k.v[e]) - m[e];
             ss = fmaf(ce, ce, ss);
         }
-        store16(Kc + base + size_t(r) * D + lane * V, c);
 #pragma unroll
         for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
         best = fmaxf(best, sqrtf(ss));
@@ -210,7 +209,6 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
     char* ws = static_cast<char*>(wsv);
     const E* Q = static_cast<const E*>(Qv);
     const E* K = static_cast<const E*>(Kv);
-    E* Kc = reinterpret_cast<E*>(ws + p.ws.kc);
     float* mu = reinterpret_cast<float*>(ws + p.ws.mu);
     float* qn = reinterpret_cast<float*>(ws + p.ws.qnorm);
     float* colsum = reinterpret_cast<float*>(ws + p.bounds.colsum);
@@ -220,8 +218,8 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
     hipLaunchKernelGGL((bounds_colsum_qnorm<E, D>), grid, dim3(256), 0, stream, Q, K, colsum, qn,
                        partqmax, N, s.T, p.bounds.rows_per_part, ppf, nparts);
     hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, N, nparts);
-    hipLaunchKernelGGL((bounds_centre<E, D>), grid, dim3(256), 0, stream, K, mu, Kc, partmax, N,
-                       s.T, p.bounds.rows_per_part, ppf, nparts);
+    hipLaunchKernelGGL((bounds_radius<E, D>), grid, dim3(256), 0, stream, K, mu, partmax, N, s.T,
+                       p.bounds.rows_per_part, ppf, nparts);
     hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, partqmax, partmax,
                        reinterpret_cast<float*>(ws + p.ws.rframe),
                        reinterpret_cast<float*>(ws + p.ws.rslice),

@@ -21,9 +21,13 @@
 //    argument. The runs are walked as one sequence in chunks of 64 keys; only
 //    the very last chunk can be shorter (16, 32 or 48 keys, a whole number of
 //    16-key granules, so still no partial block).
-//  * Per chunk, K (centred) and V are staged in LDS, double buffered with one
-//    barrier per chunk; V is written transposed so the P.V operand is a
-//    contiguous 16-byte read.
+//  * Per chunk, K and V are staged in LDS by direct-to-LDS copies, double
+//    buffered with one barrier per chunk; the V^T operand of P.V is read
+//    transposed out of row-major V (ds_read_b64_tr_b16).
+//  * Both routes score K as given. The fixed route's shift for row i is its
+//    bound on the centred scores, scale ||q_i|| R_S, plus scale q_i.mu:
+//    centring moves every score of the row by that amount, so the softmax is
+//    the same and no centred copy of K is ever stored.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: the accumulator then holds, per lane, one query
 //    and 4+4 keys, which is exactly the B-operand layout of O^T = V^T P^T, so P
@@ -50,10 +54,10 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 struct FwdArgs {
     const void* Q;
-    const void* Kc;             // centred keys (fixed-max route)
-    const void* K;              // keys as given (online route)
+    const void* K;
     const void* V;
     void* O;
+    const float* mu;            // key mean per (batch, head)
     const float* qnorm;
     const float* rslice;
     const uint8_t* elig;
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const size_t base = size_t(bh) * p.N * D;
     const __bf16* Qh = static_cast<const __bf16*>(p.Q) + base;
     const bool fixed = use_fixed(p, bh);                 // uniform per workgroup
-    const __bf16* Kh = static_cast<const __bf16*>(fixed ? p.Kc : p.K) + base;
+    const __bf16* Kh = static_cast<const __bf16*>(p.K) + base;
     const __bf16* Vh = static_cast<const __bf16*>(p.V) + base;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
 
@@ -577,11 +581,32 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 #pragma unroll
         for (int ks = 0; ks < GG::KS; ++ks)
             qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
-        shift[g] = c * (p.qnorm[size_t(bh) * p.N + row] * rsl);
+        shift[g] = p.qnorm[size_t(bh) * p.N + row] * rsl;
         rs[g] = 0.f;
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (fixed) {
+        // The fixed route scores K as given, so each row's shift is its bound
+        // on the centred scores plus q.mu (the row's whole offset from
+        // centring). The 4 lanes holding a row's columns add their partial
+        // dot products in the same pairing order, so all 4 get the same sum.
+        const float* muh = p.mu + size_t(bh) * D;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float qm = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < GG::KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    qm = fmaf(float(qf[g][ks][e]), muh[32 * ks + 8 * lj + e], qm);
+            qm += __shfl_xor(qm, 16, 64);
+            qm += __shfl_xor(qm, 32, 64);
+            shift[g] += qm;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) shift[g] *= c;
 
     if (fixed)
         attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     const size_t base = size_t(bh) * p.N * D;
     const bool fixed = use_fixed(p, bh);
     const float* Qh = static_cast<const float*>(p.Q) + base;
-    const float* Kh = static_cast<const float*>(fixed ? p.Kc : p.K) + base;
+    const float* Kh = static_cast<const float*>(p.K) + base;
     const float* Vh = static_cast<const float*>(p.V) + base;
     float* Oh = static_cast<float*>(p.O) + base;
     const float c = p.c;
@@ -628,7 +653,10 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
         q[e] = Qh[size_t(i) * D + e];
         o[e] = 0.f;
     }
-    const float shift = c * (p.qnorm[size_t(bh) * p.N + i] * p.rslice[size_t(bh) * p.F + f]);
+    float qm = 0.f;                 // the fixed route scores K as given: shift by q.mu too
+#pragma unroll
+    for (int e = 0; e < D; ++e) qm = fmaf(q[e], p.mu[size_t(bh) * D + e], qm);
+    const float shift = c * (p.qnorm[size_t(bh) * p.N + i] * p.rslice[size_t(bh) * p.F + f] + qm);
     float m = -INFINITY, rs = 0.f;
     for (int x = 0; x < sl.total; ++x) {
         const int j = sl.key(x);
@@ -673,7 +701,7 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
     const char* ws = static_cast<const char*>(wsv);
     FwdArgs a;
     a.Q = Q;
-    a.Kc = ws + p.ws.kc;
+    a.mu = reinterpret_cast<const float*>(ws + p.ws.mu);
     a.K = K;
     a.V = V;
     a.O = O;

@@ -35,7 +35,7 @@ struct BoundsGeometry {
     int32_t rows_per_part;    // key/query rows one bounds workgroup reduces
     int32_t parts_per_frame;  // ceil(T / rows_per_part)
     size_t colsum;            // private ws offsets: float [BH][F*ppf][d]
-    size_t partmax;           // float [BH][F*ppf]: max ||Kc_j|| per part
+    size_t partmax;           // float [BH][F*ppf]: max ||k_j - mu|| per part
     size_t partqmax;          // float [BH][F*ppf]: max ||q_i|| per part
 };
 

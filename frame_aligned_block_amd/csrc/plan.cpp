@@ -179,10 +179,8 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
 
         // ---- workspace layout
         const size_t BH = size_t(s.B) * s.H;
-        const size_t esz = s.dtype == FSA_BF16 ? 2 : 4;
         size_t off = 0;
         fsa_ws_layout& w = p->ws;
-        w.kc = off;      off = align_up(off + BH * N * s.d * esz);
         w.mu = off;      off = align_up(off + BH * s.d * 4);
         w.qnorm = off;   off = align_up(off + BH * N * 4);
         w.rframe = off;  off = align_up(off + BH * s.F * 4);

@@ -55,7 +55,7 @@ class fsa_shape(ctypes.Structure):
 
 
 class fsa_ws_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("kc", "mu", "qnorm", "rframe", "rslice", "stat",
+    _fields_ = [(n, c_size_t) for n in ("mu", "qnorm", "rframe", "rslice", "stat",
                                          "elig", "total")]
 
 
@@ -306,14 +306,11 @@ def workspace_views(plan: Plan, ws):
     s = fsa_plan_shape(plan)
     lay = fsa_workspace_layout(plan)
     BH, N = s.B * s.H, s.F * s.T
-    kdt = torch.bfloat16 if s.dtype == FSA_BF16 else torch.float32
-    esz = 2 if s.dtype == FSA_BF16 else 4
 
     def view(off, n, dt, sz, shape):
         return ws[off:off + n * sz].view(dt).view(*shape)
 
     return {
-        "kc": view(lay["kc"], BH * N * s.d, kdt, esz, (s.B, s.H, N, s.d)),
         "mu": view(lay["mu"], BH * s.d, torch.float32, 4, (s.B, s.H, s.d)),
         "qnorm": view(lay["qnorm"], BH * N, torch.float32, 4, (s.B, s.H, N)),
         "rframe": view(lay["rframe"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),

@@ -97,7 +97,6 @@ typedef struct fsa_plan fsa_plan;   /* opaque, host memory only */
 
 /* Byte offsets of the bound products inside a workspace. */
 typedef struct {
-    size_t kc;      /* centred keys, [B][H][N][d], the input dtype             */
     size_t mu;      /* key mean, float [B][H][d]                               */
     size_t qnorm;   /* ||q_i||, float [B][H][N]                                */
     size_t rframe;  /* max_{j in frame g} ||k_j - mu||, float [B][H][F]        */
@@ -148,10 +147,10 @@ fsa_status fsa_workspace_layout(const fsa_plan* plan, fsa_ws_layout* out);
 
 /*
  * fsa_bounds -- per (batch, head): key mean mu over all N keys (fp32, fixed
- * reduction order), centred keys Kc = round(K - mu) to the input dtype,
- * per-frame max ||Kc_j|| computed from the rounded Kc, per-slice max, row
- * norms ||q_i||, the head statistic and its eligibility flag
- * ("Unchaining the Softmax" ¶2, ¶3). Q and K are read; results go to ws.
+ * reduction order), per-frame max ||k_j - mu|| (fp32, from the keys as
+ * given), per-slice max, row norms ||q_i||, the head statistic and its
+ * eligibility flag ("Unchaining the Softmax" ¶2, ¶3). Q and K are only read
+ * (no centred copy of K is written); results go to ws.
  * scale > 0 and finite. Deterministic: no atomics, fixed reduction trees.
  * Errors: FSA_ERR_INVALID_ARG (NULL plan/pointers, bad scale),
  * FSA_ERR_WORKSPACE (ws NULL or not 256-byte aligned), FSA_ERR_HIP.
@@ -161,13 +160,14 @@ fsa_status fsa_bounds(const fsa_plan* plan, const void* Q, const void* K, void* 
 
 /*
  * fsa_forward -- the attention itself, one launch. Reads Q, K, V and the
- * bound products in ws (Kc, qnorm, rslice, elig) written by fsa_bounds for the
- * same plan, inputs and scale; writes O. Per (batch, head), mode picks the
+ * bound products in ws (mu, qnorm, rslice, elig) written by fsa_bounds for
+ * the same plan, inputs and scale; writes O. Per (batch, head), mode picks the
  * route: AUTO takes the fixed max where elig = 1 and the online softmax
- * elsewhere. The fixed-max route scores the centred keys Kc (its bound holds
- * for them); the online route is the standard one and scores the keys K as
- * given, so a loose head's large keys are never re-rounded by centring
- * ("Unchaining the Softmax" ¶3). O must not overlap Q, K, V or ws.
+ * elsewhere. Both routes score the keys as given. The fixed-max route shifts
+ * row i by its Cauchy-Schwarz bound on the centred scores plus scale q_i.mu:
+ * centring by mu moves every score of the row by that same amount, so the
+ * softmax is unchanged and the shift bounds the raw scores ("Unchaining the
+ * Softmax" ¶2, ¶3). O must not overlap Q, K, V or ws.
  * Errors: FSA_ERR_INVALID_ARG (NULL pointers, bad scale or mode, misaligned
  * tensors, O overlapping an input), FSA_ERR_WORKSPACE, FSA_ERR_HIP.
  */

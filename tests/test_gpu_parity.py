@@ -37,8 +37,8 @@ def check_bounds(run: Run, heads=None):
         assert np.max(np.abs(mu - want["mu"][0, 0])) < 1e-4, h
         qn = v["qnorm"][0, h].double().cpu().numpy()
         assert np.allclose(qn, want["qnorm"][0, 0], rtol=2e-6, atol=1e-6), h
-        # norms of the bf16-rounded centred keys vs exact centring
-        rtol = 2e-3 if cfg.dtype == "bf16" else 1e-5
+        # radii of the centred keys: fp32 from the input keys and the fp32 mean
+        rtol = 1e-5
         assert np.allclose(v["rframe"][0, h].double().cpu().numpy(), want["R"][0, 0], rtol=rtol), h
         assert np.allclose(v["rslice"][0, h].double().cpu().numpy(), want["R_S"][0, 0], rtol=rtol), h
         stat = float(v["stat"][0, h])
@@ -46,10 +46,6 @@ def check_bounds(run: Run, heads=None):
         # flags bit-exact, and every head clear of the threshold by 5%
         assert abs(want["stat"][0, 0] - orc.BETA) / orc.BETA > 0.05, (h, want["stat"])
         assert int(v["elig"][0, h]) == int(want["elig"][0, 0]), (h, stat)
-        # centred keys: exactly the input dtype's rounding of K - mu (GPU mu)
-        kc = v["kc"][0, h]
-        ref = (run.K[0, h].float() - v["mu"][0, h][None, :]).to(kc.dtype)
-        assert torch.equal(kc, ref), h
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])

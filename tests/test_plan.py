@@ -54,7 +54,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
     p = plan(13, 3600, 2, 0, 0, 0, H=24)
     lay = fsa.fsa_workspace_layout(p)
     B, H, N, d, F = 1, 24, 13 * 3600, 128, 13
-    sizes = {"kc": B * H * N * d * 2, "mu": B * H * d * 4, "qnorm": B * H * N * 4,
+    sizes = {"mu": B * H * d * 4, "qnorm": B * H * N * 4,
              "rframe": B * H * F * 4, "rslice": B * H * F * 4, "stat": B * H * 4, "elig": B * H}
     spans = sorted((lay[k], lay[k] + n) for k, n in sizes.items())
     for (a0, e0), (a1, _) in zip(spans, spans[1:]):
