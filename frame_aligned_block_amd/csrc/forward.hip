@@ -150,15 +150,14 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
                  :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Start the asynchronous global -> LDS copy of chunk ch of the slice walk (K
-// and V straight into the stage, no registers). The tile's 1 KB blocks (16
-// rows x 64 bytes of one sub-tile) are numbered j = 4i + wave; block j is
-// sub-tile j / RB, rows 16 (j % RB) .. +15, so each wave always moves the same
-// 16 rows: lane l carries row 16 (wave % RB) + l/4, 16-byte segment l%4.
-// Positions past the slice are clamped to its last key: harmless duplicates
-// that are never read, issued anyway so every chunk has the same number of
-// copies in flight.
-// Block group i (0 <= i < NI) of a chunk's copies: one K and one V copy.
+// Asynchronous global -> LDS copies of chunk ch of the slice walk (K and V
+// straight into the stage, no registers). The tile's 1 KB blocks (16 rows x
+// 64 bytes of one sub-tile) are numbered j = 4i + w for the block groups
+// i < NI and the workgroup's waves w; block j is sub-tile j / RB, rows
+// 16 (j % RB) .. +15, so the blocks of w always hold the same 16 rows: lane l
+// carries row 16 (w % RB) + l/4, 16-byte segment l%4. Positions past the
+// slice are clamped to its last key: harmless duplicates that are never read.
+// issue_group issues group i of the blocks of w: one K and one V copy.
 template <int D>
 __device__ __forceinline__ void issue_group(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                             const __bf16* Vh, int ch, int wave, int lane, int i) {
@@ -175,11 +174,23 @@ __device__ __forceinline__ void issue_group(unsigned stage_lds, const Slice& sl,
     lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * t, voff);
 }
 
+// A whole chunk's copies, issued by the first kCopyWaves waves of the
+// workgroup (wave w < kCopyWaves also issues the groups of waves w +
+// kCopyWaves, ...). A wave that issues copies stalls while the CU's address
+// path takes them; two copying waves measured about 1% faster than all four
+// (the others start their next step at once) and than one (too long a stall).
+constexpr int kCopyWaves = fsa::kWaves >= 2 ? 2 : 1;
+static_assert(fsa::kWaves % kCopyWaves == 0, "copy waves divide the workgroup");
+
 template <int D>
 __device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                             const __bf16* Vh, int ch, int wave, int lane) {
+    if (wave >= kCopyWaves) return;
 #pragma unroll
-    for (int i = 0; i < Geo<D>::NI; ++i) issue_group<D>(stage_lds, sl, Kh, Vh, ch, wave, lane, i);
+    for (int r = 0; r < fsa::kWaves / kCopyWaves; ++r)
+#pragma unroll
+        for (int i = 0; i < Geo<D>::NI; ++i)
+            issue_group<D>(stage_lds, sl, Kh, Vh, ch, wave + r * kCopyWaves, lane, i);
 }
 
 // Per-lane LDS byte offsets (constant for the whole walk).
@@ -505,10 +516,13 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
 
 // A wave that owns no query rows (past the last unit of its frame) still
 // moves its share of every chunk and passes the same barriers as the waves
-// that compute, in the same order, but issues no matrix or softmax work.
+// that compute, in the same order, but issues no matrix or softmax work. Its
+// share follows the route of the workgroup: in the loop, the fixed route
+// issues whole chunks from the copy waves and the online route has every wave
+// issue its own groups.
 template <int D>
 __device__ __forceinline__ void copy_only(unsigned char* smem, const Slice& sl, const __bf16* Kh,
-                                          const __bf16* Vh, int wave, int lane) {
+                                          const __bf16* Vh, bool fixed, int wave, int lane) {
     using GG = Geo<D>;
     const int nchunks = (sl.total + kBK - 1) / kBK;
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
@@ -520,8 +534,15 @@ __device__ __forceinline__ void copy_only(unsigned char* smem, const Slice& sl, 
     for (int ch = 0; ch + 1 < nchunks; ++ch) {
         FSA_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
-        if (ch + 2 < nchunks)
-            issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+        if (ch + 2 < nchunks) {
+            if (fixed) {
+                issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+            } else {
+#pragma unroll
+                for (int i = 0; i < GG::NI; ++i)
+                    issue_group<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane, i);
+            }
+        }
         st ^= 1;
     }
     FSA_WAIT_VMCNT(0);
@@ -566,7 +587,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     if (__builtin_amdgcn_readfirstlane(nvalid) == 0) {
-        copy_only<D>(smem, sl, Kh, Vh, uwave, lane);
+        copy_only<D>(smem, sl, Kh, Vh, fixed, uwave, lane);
         return;
     }
     const float c = p.c;
