@@ -74,6 +74,8 @@ class Config:
 # span (22x40 patches = 880 tokens) is not a multiple of 128, the 720p- and
 # 1080p-shaped super-resolution chunks (45x80 and 68x120 latent patch grids),
 # and the 720p shape with 40 heads of which one in fifty has a loose bound.
+# A sixth runs the 720p shape with a window that covers every frame: dense
+# self-attention over the chunk through the same kernel.
 CONFIGS = {
     "tiny": Config("tiny", F=5, T=48, H=2, d=64, dtype="f32", window=1,
                    ref_frame=0, shared_mean=False),
@@ -86,6 +88,8 @@ CONFIGS = {
     "stress": Config("stress", F=13, T=3600, H=40, d=128, dtype="bf16",
                      window=2, ref_frame=0, shared_mean=True, loose_period=50,
                      loose_phase=7),
+    "720p-dense": Config("720p-dense", F=13, T=3600, H=24, d=128, dtype="bf16",
+                         window=12, ref_frame=0, shared_mean=True),
 }
 
 

@@ -110,7 +110,7 @@ def test_small_bf16_full():
 # ------------------------------------------------------------------ forward, full size sampled
 
 @pytest.mark.parametrize("name,heads", [("720p", [0, 11, 23]), ("1080p", [0, 17]),
-                                        ("stress", [6, 7, 33])])
+                                        ("stress", [6, 7, 33]), ("720p-dense", [0, 13])])
 def test_full_size_sampled(name, heads):
     cfg = CONFIGS[name]
     say("forward full size", name)

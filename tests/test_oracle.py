@@ -264,7 +264,7 @@ def test_eligibility_by_construction_on_full_size_heads():
     stress config's loose head (h % 50 == 7) is not; without centring the
     normal heads would not be eligible (centring tightens the bound)."""
     margin = 1.05
-    for name, h in [("720p", 0), ("1080p", 3), ("stress", 6), ("stress", 7)]:
+    for name, h in [("720p", 0), ("1080p", 3), ("stress", 6), ("stress", 7), ("720p-dense", 0)]:
         cfg = CONFIGS[name]
         q, k, _ = make_head(cfg, 0, 0, h)
         Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
