@@ -93,7 +93,8 @@ extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const voi
         set_error("fsa_forward: scale must be finite and > 0 (got %g)", double(scale));
         return FSA_ERR_INVALID_ARG;
     }
-    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY) {
+    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
+        mode != FSA_MODE_AUTO_FRAME) {
         set_error("fsa_forward: unknown mode %d", mode);
         return FSA_ERR_INVALID_ARG;
     }
@@ -202,7 +203,8 @@ extern "C" fsa_status fsa_attention(const void* Q, const void* K, const void* V,
         set_error("fsa_attention: scale must be finite and > 0 (got %g)", double(scale));
         return FSA_ERR_INVALID_ARG;
     }
-    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY) {
+    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
+        mode != FSA_MODE_AUTO_FRAME) {
         set_error("fsa_attention: unknown mode %d", mode);
         return FSA_ERR_INVALID_ARG;
     }

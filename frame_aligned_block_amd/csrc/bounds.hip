@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void bounds_radius(
 __global__ __launch_bounds__(256) void bounds_finalize(
     const float* __restrict__ partqmax, const float* __restrict__ partmax,
     float* __restrict__ rframe, float* __restrict__ rslice, float* __restrict__ stat,
-    uint8_t* __restrict__ elig, int F, int ppf, float scale, const FrameTable tab) {
+    uint8_t* __restrict__ elig, float* __restrict__ statf, uint8_t* __restrict__ eligf, int F,
+    int ppf, float scale, const FrameTable tab) {
     __shared__ float rf[FSA_MAX_FRAMES + 1];
     __shared__ float qm[FSA_MAX_FRAMES + 1];
     __shared__ float sb[FSA_MAX_FRAMES + 1];
@@ -190,6 +191,8 @@ __global__ __launch_bounds__(256) void bounds_finalize(
         for (int g = a1; g < a1 + l1; ++g) r = fmaxf(r, rf[g]);
         rslice[size_t(bh) * F + f] = r;
         sb[f] = (scale * qm[f]) * r;
+        statf[size_t(bh) * F + f] = sb[f];
+        eligf[size_t(bh) * F + f] = sb[f] <= FSA_ELIG_BETA ? 1 : 0;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -224,7 +227,9 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
                        reinterpret_cast<float*>(ws + p.ws.rframe),
                        reinterpret_cast<float*>(ws + p.ws.rslice),
                        reinterpret_cast<float*>(ws + p.ws.stat),
-                       reinterpret_cast<uint8_t*>(ws + p.ws.elig), s.F, ppf, scale, p.table);
+                       reinterpret_cast<uint8_t*>(ws + p.ws.elig),
+                       reinterpret_cast<float*>(ws + p.ws.statf),
+                       reinterpret_cast<uint8_t*>(ws + p.ws.eligf), s.F, ppf, scale, p.table);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));

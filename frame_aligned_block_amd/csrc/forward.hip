@@ -60,7 +60,8 @@ struct FwdArgs {
     const float* mu;            // key mean per (batch, head)
     const float* qnorm;
     const float* rslice;
-    const uint8_t* elig;
+    const uint8_t* elig;        // per (batch, head)
+    const uint8_t* eligf;       // per (batch, head, frame)
     float c;                    // scale * log2(e)
     int32_t N, T, F, BH;
     int32_t units_per_frame;    // row units of 16*G rows per frame
@@ -97,9 +98,10 @@ __device__ __forceinline__ Slice slice_of(const FrameTable& t, int f, int T) {
     return s;
 }
 
-__device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh) {
+__device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh, int f) {
     if (p.mode == FSA_MODE_FIXED_ONLY) return true;
     if (p.mode == FSA_MODE_ONLINE_ONLY) return false;
+    if (p.mode == FSA_MODE_AUTO_FRAME) return p.eligf[size_t(bh) * p.F + f] != 0;
     return p.elig[bh] != 0;
 }
 
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 
     const size_t base = size_t(bh) * p.N * D;
     const __bf16* Qh = static_cast<const __bf16*>(p.Q) + base;
-    const bool fixed = use_fixed(p, bh);                 // uniform per workgroup
+    const bool fixed = use_fixed(p, bh, f);              // uniform per workgroup
     const __bf16* Kh = static_cast<const __bf16*>(p.K) + base;
     const __bf16* Vh = static_cast<const __bf16*>(p.V) + base;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
@@ -661,7 +663,7 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     const int T = p.T, f = i / T;
     const Slice sl = slice_of(p.tab, f, T);
     const size_t base = size_t(bh) * p.N * D;
-    const bool fixed = use_fixed(p, bh);
+    const bool fixed = use_fixed(p, bh, f);
     const float* Qh = static_cast<const float*>(p.Q) + base;
     const float* Kh = static_cast<const float*>(p.K) + base;
     const float* Vh = static_cast<const float*>(p.V) + base;
@@ -729,6 +731,7 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
     a.qnorm = reinterpret_cast<const float*>(ws + p.ws.qnorm);
     a.rslice = reinterpret_cast<const float*>(ws + p.ws.rslice);
     a.elig = reinterpret_cast<const uint8_t*>(ws + p.ws.elig);
+    a.eligf = reinterpret_cast<const uint8_t*>(ws + p.ws.eligf);
     a.c = scale * kLog2e;
     a.N = s.F * s.T;
     a.T = s.T;

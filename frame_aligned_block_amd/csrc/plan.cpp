@@ -187,6 +187,8 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         w.rslice = off;  off = align_up(off + BH * s.F * 4);
         w.stat = off;    off = align_up(off + BH * 4);
         w.elig = off;    off = align_up(off + BH);
+        w.statf = off;   off = align_up(off + BH * s.F * 4);
+        w.eligf = off;   off = align_up(off + BH * s.F);
         const size_t nparts = size_t(s.F) * p->bounds.parts_per_frame;
         p->bounds.colsum = off;  off = align_up(off + BH * nparts * s.d * 4);
         p->bounds.partmax = off; off = align_up(off + BH * nparts * 4);

@@ -34,7 +34,9 @@ FSA_F32 = 1
 FSA_MODE_AUTO = 0
 FSA_MODE_ONLINE_ONLY = 1
 FSA_MODE_FIXED_ONLY = 2
-MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MODE_FIXED_ONLY}
+FSA_MODE_AUTO_FRAME = 3
+MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MODE_FIXED_ONLY,
+         "auto_frame": FSA_MODE_AUTO_FRAME}
 
 FSA_ELIG_BETA = 32.0
 FSA_MAX_FRAMES = 255
@@ -56,7 +58,7 @@ class fsa_shape(ctypes.Structure):
 
 class fsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("mu", "qnorm", "rframe", "rslice", "stat",
-                                         "elig", "total")]
+                                         "elig", "statf", "eligf", "total")]
 
 
 class FsaError(RuntimeError):
@@ -317,4 +319,6 @@ def workspace_views(plan: Plan, ws):
         "rslice": view(lay["rslice"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
         "stat": view(lay["stat"], BH, torch.float32, 4, (s.B, s.H)),
         "elig": view(lay["elig"], BH, torch.uint8, 1, (s.B, s.H)),
+        "statf": view(lay["statf"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
+        "eligf": view(lay["eligf"], BH * s.F, torch.uint8, 1, (s.B, s.H, s.F)),
     }

@@ -18,8 +18,8 @@ regenerated without drawing the others):
       v = N(0,1) [N, d];
       p = randint(0, T) [F]        (only for a loose head);
   * k = e + c  (or k = e);
-  * a loose head multiplies, in every frame g, the raw key at token g*T + p[g]
-    (shared mean included) by 20;
+  * a loose head multiplies, in every frame g (or only in the frames a config
+    lists), the raw key at token g*T + p[g] (shared mean included) by 20;
   * finally q, k, v are cast to the config dtype (bf16 rounds to nearest even).
 The cast tensors are the inputs; the oracle upcasts exactly these values.
 
@@ -47,6 +47,7 @@ class Config:
     shared_mean: bool  # keys = c + N(0,1) with one c ~ N(0, 4^2) per head
     loose_period: int = 0   # head h is loose iff loose_period and h % loose_period == loose_phase
     loose_phase: int = 0
+    loose_frames: tuple = ()  # frames holding a loose head's outlier key; () = every frame
     B: int = 1
 
     @property
@@ -75,7 +76,10 @@ class Config:
 # 1080p-shaped super-resolution chunks (45x80 and 68x120 latent patch grids),
 # and the 720p shape with 40 heads of which one in fifty has a loose bound.
 # A sixth runs the 720p shape with a window that covers every frame: dense
-# self-attention over the chunk through the same kernel.
+# self-attention over the chunk through the same kernel. A seventh has loose
+# heads whose outlier key sits in one frame only (frame 6), so only the frames
+# whose slice holds frame 6 have a loose bound: the case for eligibility per
+# (head, frame).
 CONFIGS = {
     "tiny": Config("tiny", F=5, T=48, H=2, d=64, dtype="f32", window=1,
                    ref_frame=0, shared_mean=False),
@@ -90,6 +94,9 @@ CONFIGS = {
                      loose_phase=7),
     "720p-dense": Config("720p-dense", F=13, T=3600, H=24, d=128, dtype="bf16",
                          window=12, ref_frame=0, shared_mean=True),
+    "outlier-frame": Config("outlier-frame", F=13, T=3600, H=8, d=128, dtype="bf16",
+                            window=2, ref_frame=0, shared_mean=True, loose_period=4,
+                            loose_phase=1, loose_frames=(6,)),
 }
 
 
@@ -112,6 +119,8 @@ def make_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
     if cfg.is_loose(h):
         p = torch.randint(0, cfg.T, (cfg.F,), generator=g, device=device)
         rows = torch.arange(cfg.F, device=device) * cfg.T + p
+        if cfg.loose_frames:
+            rows = rows[list(cfg.loose_frames)]
         k[rows] *= 20.0
     dt = cfg.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)

@@ -72,8 +72,11 @@ typedef enum { FSA_BF16 = 0, FSA_F32 = 1 } fsa_dtype;
 typedef enum {
     FSA_MODE_AUTO = 0,          /* per head: fixed max if eligible, else online */
     FSA_MODE_ONLINE_ONLY = 1,   /* every head online (the A/B baseline)         */
-    FSA_MODE_FIXED_ONLY = 2     /* every head fixed max (tests: shows why the
+    FSA_MODE_FIXED_ONLY = 2,    /* every head fixed max (tests: shows why the
                                    fallback exists; loose heads underflow)      */
+    FSA_MODE_AUTO_FRAME = 3     /* per (head, frame): fixed max where every row of
+                                   the frame has its bound within FSA_ELIG_BETA,
+                                   else online                                   */
 } fsa_mode;
 
 /* Eligibility threshold on a head's largest row bound, in logit units. */
@@ -103,6 +106,9 @@ typedef struct {
     size_t rslice;  /* max over the frames of S(f) of rframe, float [B][H][F]  */
     size_t stat;    /* scale * max_i ||q_i|| rslice(f(i)), float [B][H]        */
     size_t elig;    /* 1 if stat <= FSA_ELIG_BETA else 0, uint8 [B][H]         */
+    size_t statf;   /* per frame f: scale * max_{i in f} ||q_i|| rslice(f),
+                       float [B][H][F]                                         */
+    size_t eligf;   /* 1 if statf <= FSA_ELIG_BETA else 0, uint8 [B][H][F]     */
     size_t total;   /* bytes needed (== fsa_workspace_bytes)                   */
 } fsa_ws_layout;
 
@@ -163,7 +169,11 @@ fsa_status fsa_bounds(const fsa_plan* plan, const void* Q, const void* K, void* 
  * bound products in ws (mu, qnorm, rslice, elig) written by fsa_bounds for
  * the same plan, inputs and scale; writes O. Per (batch, head), mode picks the
  * route: AUTO takes the fixed max where elig = 1 and the online softmax
- * elsewhere. Both routes score the keys as given. The fixed-max route shifts
+ * elsewhere (the per-head check of "Unchaining the Softmax" ¶3); AUTO_FRAME
+ * decides per (batch, head, frame) from eligf instead, a finer check that is
+ * as safe (every row of the frame has its bound within FSA_ELIG_BETA) and
+ * keeps the frames of a loose head that never see its outlier keys on the
+ * fixed route. Both routes score the keys as given. The fixed-max route shifts
  * row i by its Cauchy-Schwarz bound on the centred scores plus scale q_i.mu:
  * centring by mu moves every score of the row by that same amount, so the
  * softmax is unchanged and the shift bounds the raw scores ("Unchaining the

@@ -149,7 +149,10 @@ def bounds(Q, K, F: int, T: int, window: int, ref_frame: int, scale: float,
     ``centre=False`` computes the same statistics on the raw keys.
     Returns mu [B,H,d], qnorm [B,H,N], R [B,H,F] (max centred key norm per
     frame), R_S [B,H,F] (max over the slice of frame f), bound [B,H,N],
-    stat [B,H] and elig [B,H] (bool).
+    stat [B,H] and elig [B,H] (bool), and the same check per (head, frame):
+    stat_frame [B,H,F] (the largest row bound among the frame's rows) and
+    elig_frame [B,H,F] (bool). A frame passes when each of its rows does, so
+    the finer check carries the same guarantee row by row.
     """
     Q = _f64(Q)
     K = _f64(K)
@@ -169,8 +172,10 @@ def bounds(Q, K, F: int, T: int, window: int, ref_frame: int, scale: float,
     frame_of_row = np.arange(N) // T
     bound = scale * qnorm * R_S[:, :, frame_of_row]
     stat = bound.max(axis=-1)
+    stat_frame = bound.reshape(B, H, F, T).max(axis=-1)
     return {"mu": mu, "qnorm": qnorm, "R": R, "R_S": R_S, "bound": bound,
-            "stat": stat, "elig": stat <= beta}
+            "stat": stat, "elig": stat <= beta,
+            "stat_frame": stat_frame, "elig_frame": stat_frame <= beta}
 
 
 # --------------------------------------------------------------------------

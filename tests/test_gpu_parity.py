@@ -149,6 +149,50 @@ def test_auto_vs_online_ab():
         assert_close(cfg, Oa[0, h, rows], want, f"ab head {h}")
 
 
+def test_frame_eligibility_and_auto_frame():
+    """Per (head, frame) route (AUTO_FRAME) on the outlier-frame workload:
+    the frame statistics and flags match the oracle (flags bit-exact); the
+    loose heads' frames that never see the outlier take the fixed max, the
+    others the online route bit-identically to ONLINE_ONLY; normal heads are
+    bit-identical to AUTO; sampled rows of every frame meet the bf16 bar."""
+    cfg = CONFIGS["outlier-frame"]
+    say("frame eligibility", cfg.name)
+    run = Run(cfg).bounds()
+    torch.cuda.synchronize()
+    v = run.views()
+    for h in (0, 1, 5):
+        q = to_f64(run.Q[0, h])[None, None]
+        k = to_f64(run.K[0, h])[None, None]
+        want = orc.bounds(q, k, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        sf = v["statf"][0, h].double().cpu().numpy()
+        assert np.allclose(sf, want["stat_frame"][0, 0], rtol=1e-5), h
+        assert np.all(np.abs(want["stat_frame"][0, 0] - orc.BETA) / orc.BETA > 0.05), h
+        assert np.array_equal(v["eligf"][0, h].cpu().numpy().astype(bool),
+                              want["elig_frame"][0, 0]), h
+    eligf = v["eligf"][0].cpu().numpy()
+    assert eligf[[0, 2, 3, 4, 6, 7]].all() and eligf[[1, 5]].sum() == 2 * 8
+    Of = run.forward("auto_frame")
+    Oa = run.forward("auto")
+    Oo = run.forward("online")
+    T = cfg.T
+    for h in range(cfg.H):
+        if cfg.is_loose(h):
+            for f in range(cfg.F):
+                blk = slice(f * T, (f + 1) * T)
+                if eligf[h, f]:
+                    d = (Of[0, h, blk].float() - Oo[0, h, blk].float()).abs()
+                    assert float(d.max()) <= BF16_MAX_ABS, (h, f)
+                else:
+                    assert torch.equal(Of[0, h, blk], Oo[0, h, blk]), (h, f)
+        else:
+            assert torch.equal(Of[0, h], Oa[0, h]), h
+    for h in (0, 1):
+        rows = sample_rows(cfg, 150, seed=h)
+        want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+        mx, mean = assert_close(cfg, Of[0, h, rows], want, f"auto_frame head {h}")
+        print(f"auto_frame h{h}: max {mx:.3g} mean {mean:.3g}")
+
+
 def test_fixed_only_on_a_loose_head_breaks():
     """Negative control: forcing the fixed max on a loose head underflows."""
     cfg = CONFIGS["stress"].with_(F=6, T=720, H=3, loose_period=3, loose_phase=1)

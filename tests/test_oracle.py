@@ -281,6 +281,31 @@ def test_eligibility_by_construction_on_full_size_heads():
             assert raw["stat"][0, 0] > orc.BETA * margin, (name, h, raw["stat"])
 
 
+def test_frame_eligibility_follows_the_outlier_frame():
+    """Per (head, frame) eligibility on the outlier-frame workload: a loose
+    head's outlier keys sit in frame 6 only, so exactly the frames whose slice
+    (window +-2, reference frame 0) holds frame 6 fail, by a wide margin, and
+    every other frame passes, as do all frames of a normal head; the head-level
+    flag is their conjunction."""
+    cfg = CONFIGS["outlier-frame"]
+    margin = 1.05
+    for h in (0, 1):
+        q, k, _ = make_head(cfg, 0, 0, h)
+        Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+        b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        sees_outlier = [6 in orc.slice_frames(cfg.F, cfg.window, cfg.ref_frame, f)
+                        for f in range(cfg.F)]
+        assert sees_outlier == [f in (4, 5, 6, 7, 8) for f in range(cfg.F)]
+        for f in range(cfg.F):
+            sf = b["stat_frame"][0, 0, f]
+            if cfg.is_loose(h) and sees_outlier[f]:
+                assert sf > orc.BETA * margin and not b["elig_frame"][0, 0, f], (h, f, sf)
+            else:
+                assert sf < orc.BETA / margin and b["elig_frame"][0, 0, f], (h, f, sf)
+        assert b["stat"][0, 0] == b["stat_frame"][0, 0].max()
+        assert bool(b["elig"][0, 0]) == bool(b["elig_frame"][0, 0].all())
+
+
 # ---------------------------------------------------------------- routes
 
 def test_fixed_max_and_online_routes_equal_the_definition():

@@ -55,7 +55,8 @@ def test_workspace_layout_is_aligned_and_disjoint():
     lay = fsa.fsa_workspace_layout(p)
     B, H, N, d, F = 1, 24, 13 * 3600, 128, 13
     sizes = {"mu": B * H * d * 4, "qnorm": B * H * N * 4,
-             "rframe": B * H * F * 4, "rslice": B * H * F * 4, "stat": B * H * 4, "elig": B * H}
+             "rframe": B * H * F * 4, "rslice": B * H * F * 4, "stat": B * H * 4, "elig": B * H,
+             "statf": B * H * F * 4, "eligf": B * H * F}
     spans = sorted((lay[k], lay[k] + n) for k, n in sizes.items())
     for (a0, e0), (a1, _) in zip(spans, spans[1:]):
         assert e0 <= a1
