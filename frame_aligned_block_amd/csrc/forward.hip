@@ -105,6 +105,44 @@ __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh, int f) {
     return p.elig[bh] != 0;
 }
 
+// Whether the (batch*head, frame) pairs of this launch take different routes
+// (then their costs differ by the online route's ~1.3x). Every workgroup reads
+// the same flags and reaches the same answer; launches past kMixScan pairs
+// are treated as uniform.
+constexpr int kMixScan = 4096;
+
+__device__ __forceinline__ bool routes_mixed(const FwdArgs& p) {
+    const uint8_t* fl;
+    int n;
+    if (p.mode == FSA_MODE_AUTO) {
+        fl = p.elig;
+        n = p.BH;
+    } else if (p.mode == FSA_MODE_AUTO_FRAME) {
+        fl = p.eligf;
+        n = p.BH * p.F;
+    } else {
+        return false;
+    }
+    if (n > kMixScan) return false;
+    const uint8_t first = fl[0];
+    int diff = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) diff |= fl[i] != first;
+    return __syncthreads_or(diff) != 0;
+}
+
+// The pair of the ti-th place in the launch order. Uniform launches walk the
+// pairs in order, so each XCD (a contiguous range of places) holds whole heads
+// with their frames side by side and shares their key slices in its L2. Mixed
+// launches deal the pairs out x, x+8, x+16, ... for x = 0..7, so each XCD gets
+// its share of the online pairs. A bijection on [0, BH*F).
+__device__ __forceinline__ int pair_at(const FwdArgs& p, int ti, bool mixed) {
+    if (!mixed) return ti;
+    const int P = p.BH * p.F, q8 = P >> 3, r8 = P & 7;
+    if (ti < r8 * (q8 + 1)) return ti / (q8 + 1) + 8 * (ti % (q8 + 1));
+    const int j = ti - r8 * (q8 + 1);
+    return r8 + j / q8 + 8 * (j % q8);            // here q8 >= 1
+}
+
 // ---------------------------------------------------------------- bf16 route
 
 #ifndef FSA_CHUNK_KEYS
@@ -566,7 +604,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 
     const int L = xcd_remap(blockIdx.x, p.nwg);
     const int gq = L % p.groups_per_frame;
-    const int t1 = L / p.groups_per_frame;
+    const int t1 = pair_at(p, L / p.groups_per_frame, routes_mixed(p));
     const int f = frame_at(p.tab, t1 % p.F);
     const int bh = t1 / p.F;
     const int T = p.T;
