@@ -49,6 +49,7 @@ class Config:
     loose_phase: int = 0
     loose_frames: tuple = ()  # frames holding a loose head's outlier key; () = every frame
     B: int = 1
+    M: int = 0        # cross-attention: reference tokens every query attends to (0 = self)
 
     @property
     def N(self) -> int:
@@ -79,7 +80,10 @@ class Config:
 # self-attention over the chunk through the same kernel. A seventh has loose
 # heads whose outlier key sits in one frame only (frame 6), so only the frames
 # whose slice holds frame 6 have a loose bound: the case for eligibility per
-# (head, frame).
+# (head, frame). The last two are cross-attention: every token of the chunk
+# attends to the M tokens of a separate reference set (one 3600-token
+# reference image at 720p; 720 tokens in the small case, whose head 3 has a
+# loose reference key), through the same kernel.
 CONFIGS = {
     "tiny": Config("tiny", F=5, T=48, H=2, d=64, dtype="f32", window=1,
                    ref_frame=0, shared_mean=False),
@@ -97,6 +101,11 @@ CONFIGS = {
     "outlier-frame": Config("outlier-frame", F=13, T=3600, H=8, d=128, dtype="bf16",
                             window=2, ref_frame=0, shared_mean=True, loose_period=4,
                             loose_phase=1, loose_frames=(6,)),
+    "720p-xref": Config("720p-xref", F=13, T=3600, H=24, d=128, dtype="bf16", window=0,
+                        ref_frame=0, shared_mean=True, M=3600),
+    "xref-small": Config("xref-small", F=4, T=880, H=4, d=128, dtype="bf16", window=0,
+                         ref_frame=0, shared_mean=True, M=720, loose_period=4,
+                         loose_phase=3),
 }
 
 
@@ -126,15 +135,40 @@ def make_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
     return q.to(dt), k.to(dt), v.to(dt)
 
 
+def make_cross_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
+    """Draw one head's (q, kr, vr) of a cross-attention workload: q [N, d] for
+    the chunk's tokens, kr and vr [M, d] for the reference tokens. Draw order:
+    q = N(0,1); e = N(0,1) [M, d]; c = 4 N(0,1) [1, d] (shared-mean configs);
+    vr = N(0,1) [M, d]; a loose head then multiplies the reference key at a
+    seeded position p = randint(0, M) by 20. kr = e + c."""
+    g = torch.Generator(device=device)
+    g.manual_seed(head_seed(seed, b, h))
+    N, M, d = cfg.N, cfg.M, cfg.d
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((N, d), **kw)
+    k = torch.randn((M, d), **kw)
+    if cfg.shared_mean:
+        k += 4.0 * torch.randn((1, d), **kw)
+    v = torch.randn((M, d), **kw)
+    if cfg.is_loose(h):
+        p = int(torch.randint(0, M, (1,), generator=g, device=device))
+        k[p] *= 20.0
+    dt = cfg.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
 def make_inputs(cfg: Config, seed: int = 0, device="cpu"):
-    """Draw Q, K, V of shape [B, H, N, d] (contiguous) in the config dtype."""
+    """Draw Q, K, V (contiguous, the config dtype): Q [B, H, N, d]; K and V
+    [B, H, N, d], or [B, H, M, d] for a cross-attention workload (M > 0)."""
     shape = (cfg.B, cfg.H, cfg.N, cfg.d)
     Q = torch.empty(shape, dtype=cfg.torch_dtype, device=device)
-    K = torch.empty_like(Q)
-    V = torch.empty_like(Q)
+    kshape = (cfg.B, cfg.H, cfg.M, cfg.d) if cfg.M else shape
+    K = torch.empty(kshape, dtype=cfg.torch_dtype, device=device)
+    V = torch.empty_like(K)
+    draw = make_cross_head if cfg.M else make_head
     for b in range(cfg.B):
         for h in range(cfg.H):
-            q, k, v = make_head(cfg, seed, b, h, device)
+            q, k, v = draw(cfg, seed, b, h, device)
             Q[b, h], K[b, h], V[b, h] = q, k, v
     return Q, K, V
 

@@ -36,7 +36,9 @@ Pins (tests that tie this module to facts other than itself): brute-force
 masks and explicit loops, torch's scaled_dot_product_attention on the CPU in
 float64, centring invariance, the bound against the true row max, closed-form
 slice sizes and structured value probes. No function here is parity
-unpinned.
+unpinned. The cross-attention functions at the end are pinned the same way:
+torch's scaled_dot_product_attention, invariance to a shared key offset,
+constant values, and the bound against the true row max.
 """
 from __future__ import annotations
 
@@ -305,3 +307,57 @@ def attention_two_pass(Q, K, V, F, T, window, ref_frame, scale, b, h, rows,
         lse = np.logaddexp.reduce(lses)
         out[n] = sum(np.exp(l_ - lse) * o for l_, o in zip(lses, outs))
     return out
+
+
+# --------------------------------------------------------------------------
+# cross-attention to a reference token set: another attention variant of the
+# pipeline ("The Workload, and the Port" ¶3: each attention variant gets a
+# kernel built for its shape; the product conditions on one photo)
+# --------------------------------------------------------------------------
+
+def cross_attention_rows(Q, Kr, Vr, scale: float, b: int, h: int, rows) -> np.ndarray:
+    """Rows ``rows`` of O[b, h] for cross-attention: every query row attends
+    to all M reference tokens, O_i = softmax_j(scale <q_i, kr_j>) vr. Float64."""
+    rows = np.asarray(rows, dtype=np.int64)
+    k = _f64(Kr[b, h])
+    v = _f64(Vr[b, h])
+    out = np.empty((rows.size, k.shape[1]))
+    for c in range(0, rows.size, ROW_CHUNK):
+        part = rows[c:c + ROW_CHUNK]
+        out[c:c + ROW_CHUNK] = _softmax_rows(_f64(Q[b, h][part]), k, v, scale)
+    return out
+
+
+def cross_attention(Q, Kr, Vr, scale: float) -> np.ndarray:
+    """Full cross-attention output [B, H, N, d] in float64."""
+    B, H, N, d = Q.shape
+    O = np.empty((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            O[b, h] = cross_attention_rows(Q, Kr, Vr, scale, b, h, np.arange(N))
+    return O
+
+
+def cross_bounds(Q, Kr, F: int, T: int, scale: float, beta: float = BETA) -> dict:
+    """Cauchy-Schwarz bounds of cross-attention. The reference keys are
+    centred on their own mean mu (softmax-invariant: the row's logits all move
+    by scale <q_i, mu>); every row sees every reference key, so its bound is
+    scale ||q_i|| R with R = max_j ||kr_j - mu|| ("Unchaining the Softmax"
+    ¶2-¶3). Eligibility per head (stat = max_i bound_i <= beta) and per query
+    frame (stat_frame over the frame's rows), as for self-attention.
+    Returns mu [B,H,d], qnorm [B,H,N], R [B,H], bound [B,H,N], stat, elig,
+    stat_frame [B,H,F], elig_frame."""
+    Q = _f64(Q)
+    Kr = _f64(Kr)
+    B, H, N, d = Q.shape
+    assert N == F * T
+    mu = Kr.mean(axis=-2)
+    kc = Kr - mu[:, :, None, :]
+    R = np.sqrt(np.einsum("bhmd,bhmd->bhm", kc, kc)).max(axis=-1)
+    qnorm = np.sqrt(np.einsum("bhnd,bhnd->bhn", Q, Q))
+    bound = scale * qnorm * R[:, :, None]
+    stat = bound.max(axis=-1)
+    stat_frame = bound.reshape(B, H, F, T).max(axis=-1)
+    return {"mu": mu, "qnorm": qnorm, "R": R, "bound": bound, "stat": stat,
+            "elig": stat <= beta, "stat_frame": stat_frame,
+            "elig_frame": stat_frame <= beta}

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from oracle import fsa_oracle as orc
-from frame_aligned_block_amd.inputs import CONFIGS, make_head, make_inputs, to_f64
+from frame_aligned_block_amd.inputs import CONFIGS, make_cross_head, make_head, make_inputs, to_f64
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "slice_sizes.json")
 
@@ -369,3 +369,67 @@ def test_structured_value_probes():
         sel = (np.abs(frame - f) <= w) | (frame == r)
         want = V4[0, 0][sel].mean(axis=0)
         assert np.max(np.abs(O4[f * T:(f + 1) * T] - want)) < 1e-13
+
+
+# ---------------------------------------------------------------- cross-attention
+
+def test_cross_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(11)
+    B, H, N, M, d = 1, 2, 96, 48, 32
+    Q = rng.standard_normal((B, H, N, d))
+    Kr = rng.standard_normal((B, H, M, d)) + 3.0 * rng.standard_normal((B, H, 1, d))
+    Vr = rng.standard_normal((B, H, M, d))
+    scale = 1 / math.sqrt(d)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(Kr), torch.from_numpy(Vr), scale=scale).numpy()
+    assert np.max(np.abs(orc.cross_attention(Q, Kr, Vr, scale) - want)) < 1e-12
+    rows = np.array([0, 5, 95, 40])
+    part = orc.cross_attention_rows(Q, Kr, Vr, scale, 0, 1, rows)
+    assert np.max(np.abs(part - want[0, 1, rows])) < 1e-12
+
+
+def test_cross_attention_invariances_and_bound():
+    """A shared offset on every reference key leaves the output unchanged
+    (each row's logits move together); constant values pass through; the
+    bound of every row is at least its largest centred logit, and is reached
+    when the query is parallel to the longest centred key."""
+    rng = np.random.default_rng(12)
+    F, T, M, d = 3, 16, 32, 16
+    N = F * T
+    Q = rng.standard_normal((1, 1, N, d))
+    Kr = rng.standard_normal((1, 1, M, d))
+    Vr = rng.standard_normal((1, 1, M, d))
+    base = orc.cross_attention(Q, Kr, Vr, 0.3)
+    shifted = orc.cross_attention(Q, Kr + 5.0 * rng.standard_normal((1, 1, 1, d)), Vr, 0.3)
+    assert np.max(np.abs(base - shifted)) < 1e-12
+    ones = orc.cross_attention(Q, Kr, np.ones((1, 1, M, d)), 0.3)
+    assert np.max(np.abs(ones - 1.0)) < 1e-14
+    b = orc.cross_bounds(Q, Kr, F, T, 0.3)
+    kc = Kr[0, 0] - Kr[0, 0].mean(axis=0)
+    logits = 0.3 * (Q[0, 0] @ kc.T)
+    assert np.all(b["bound"][0, 0] >= logits.max(axis=1) - 1e-12)
+    j = int(np.argmax(np.linalg.norm(kc, axis=1)))
+    Q2 = Q.copy()
+    Q2[0, 0, 7] = 0.5 * kc[j]
+    b2 = orc.cross_bounds(Q2, Kr, F, T, 0.3)
+    assert b2["bound"][0, 0, 7] == pytest.approx((0.3 * (Q2[0, 0, 7] @ kc.T)).max(), rel=1e-13)
+    assert b["stat"][0, 0] == b["stat_frame"][0, 0].max()
+
+
+def test_cross_eligibility_by_construction():
+    """A normal cross head (reference keys with a shared mean) is eligible once
+    centred and not without centring; the small cross workload's head 3, with
+    one reference key scaled by 20, is not."""
+    margin = 1.05
+    for name, h in [("720p-xref", 0), ("xref-small", 0), ("xref-small", 3)]:
+        cfg = CONFIGS[name]
+        q, k, _ = make_cross_head(cfg, 0, 0, h)
+        Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+        b = orc.cross_bounds(Q, K, cfg.F, cfg.T, cfg.scale)
+        stat = b["stat"][0, 0]
+        if cfg.is_loose(h):
+            assert stat > orc.BETA * margin and not b["elig"][0, 0], (name, h, stat)
+        else:
+            assert stat < orc.BETA / margin and b["elig"][0, 0], (name, h, stat)
+            raw = cfg.scale * np.linalg.norm(Q[0, 0], axis=1).max() * np.linalg.norm(K[0, 0], axis=1).max()
+            assert raw > orc.BETA * margin, (name, h, raw)
