@@ -82,6 +82,10 @@ def cpu_baseline(cfg, Q, K, V, seconds: float):
     frames = sorted(range(cfg.F), key=lambda f: -len(orc.slice_frames(cfg.F, cfg.window,
                                                                        cfg.ref_frame, f)))
     units = [(h, f) for f in frames for h in range(cfg.H)]
+
+    def keys_of(f):       # keys a query of frame f attends to
+        return cfg.M if cfg.M else cfg.T * len(orc.slice_frames(cfg.F, cfg.window,
+                                                                cfg.ref_frame, f))
     cache = {}
     flops = 0.0
     spent = 0.0
@@ -95,17 +99,27 @@ def cpu_baseline(cfg, Q, K, V, seconds: float):
         q, k, v = cache[h]
         rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
         t0 = time.perf_counter()
-        orc.attention_rows(q, k, v, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0, 0,
-                           rows)
+        if cfg.M:
+            orc.cross_attention_rows(q, k, v, cfg.scale, 0, 0, rows)
+        else:
+            orc.attention_rows(q, k, v, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0,
+                               0, rows)
         spent += time.perf_counter() - t0
-        flops += 4.0 * cfg.d * cfg.T * cfg.T * len(orc.slice_frames(cfg.F, cfg.window,
-                                                                    cfg.ref_frame, f))
+        flops += 4.0 * cfg.d * cfg.T * keys_of(f)
         n += 1
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} (head, query-frame) blocks of {cfg.T} rows each of the {cfg.name} "
                       f"workload (heaviest frames first), {flops / 1e9:.0f} valid GFLOP in "
                       f"{spent:.1f} s; fp64 numpy, BLAS on {threads} threads"}
+
+
+def workload_name(cfg) -> str:
+    head = (f"{cfg.name}-shaped SR chunk: F={cfg.F} frames x T={cfg.T} tokens ({cfg.N} "
+            f"tokens), H={cfg.H}, d={cfg.d}, {cfg.dtype}, ")
+    if cfg.M:
+        return head + f"cross-attention of every token to M={cfg.M} reference tokens"
+    return head + f"window +-{cfg.window} + reference frame {cfg.ref_frame}"
 
 
 def current_sclk_mhz():
@@ -167,8 +181,12 @@ def main() -> int:
     print(f"[bench] {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
     Q, K, V = make_inputs(cfg, seed=0, device="cuda")
     code = fsa.FSA_BF16 if cfg.dtype == "bf16" else fsa.FSA_F32
-    plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
-                                              cfg.ref_frame, args.bq, 0, code))
+    if cfg.M:           # cross-attention to M reference tokens
+        plan = fsa.fsa_plan_create_cross(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, 0, 0,
+                                                        args.bq, 0, code), cfg.M)
+    else:
+        plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d,
+                                                  cfg.window, cfg.ref_frame, args.bq, 0, code))
     ws = torch.zeros(fsa.fsa_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     O = torch.empty_like(Q)
     pairs = fsa.fsa_plan_valid_pairs(plan)
@@ -237,10 +255,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped SR chunk: F={cfg.F} frames x T={cfg.T} "
-                               f"tokens ({cfg.N} tokens), H={cfg.H}, d={cfg.d}, {cfg.dtype}, "
-                               f"window +-{cfg.window} + reference frame {cfg.ref_frame}",
+        "config": {"workload": workload_name(cfg),
                    "B": cfg.B, "H": cfg.H, "F": cfg.F, "T": cfg.T, "d": cfg.d,
+                   **({"M": cfg.M} if cfg.M else {}),
                    "mode": args.mode, "bq": fsa.fsa_plan_shape(plan).bq,
                    "valid_pairs_per_head": pairs, "valid_flops_per_step": flops},
         "ms_per_call": round(ms_step, 4),

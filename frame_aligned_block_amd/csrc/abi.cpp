@@ -34,9 +34,18 @@ bool good_scale(float scale) { return std::isfinite(scale) && scale > 0.0f; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+size_t elem_bytes(const fsa_plan& p) { return p.shape.dtype == FSA_BF16 ? 2 : 4; }
+
+// Bytes of Q or O: [B][H][F*T][d].
 size_t tensor_bytes(const fsa_plan& p) {
     const fsa_shape& s = p.shape;
-    return size_t(s.B) * s.H * s.F * s.T * s.d * (s.dtype == FSA_BF16 ? 2 : 4);
+    return size_t(s.B) * s.H * s.F * s.T * s.d * elem_bytes(p);
+}
+
+// Bytes of K or V: [B][H][key tokens][d] (F*T, or M for a cross plan).
+size_t kv_bytes(const fsa_plan& p) {
+    const fsa_shape& s = p.shape;
+    return size_t(s.B) * s.H * size_t(p.key_tokens()) * s.d * elem_bytes(p);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -106,8 +115,8 @@ extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const voi
         set_error("fsa_forward: workspace missing or not 256-byte aligned");
         return FSA_ERR_WORKSPACE;
     }
-    const size_t nb = tensor_bytes(*plan);
-    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
+    const size_t nb = tensor_bytes(*plan), kb = kv_bytes(*plan);
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, kb) || overlaps(O, nb, V, kb) ||
         overlaps(O, nb, ws, plan->ws.total)) {
         set_error("fsa_forward: O overlaps Q, K, V or the workspace");
         return FSA_ERR_INVALID_ARG;
@@ -138,14 +147,17 @@ extern "C" fsa_status fsa_copy_eligibility(const fsa_plan* plan, const void* ws,
 
 namespace {
 
-using Key = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t>;
+// (B, H, F, T, d, window, ref_frame, dtype, M); M = 0 for self-attention.
+using Key = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
+                       int32_t>;
 
 std::mutex g_cache_mu;
 std::map<Key, fsa_plan*> g_cache;
 
-// Looks up or builds the plan of a shape (bq = bk = 0). Caller holds no lock.
-fsa_status cached_plan(const fsa_shape& s, const fsa_plan** out) {
-    const Key key{s.B, s.H, s.F, s.T, s.d, s.window, s.ref_frame, s.dtype};
+// Looks up or builds the plan of a shape (bq = bk = 0; M > 0: a cross plan).
+// Caller holds no lock.
+fsa_status cached_plan(const fsa_shape& s, int32_t M, const fsa_plan** out) {
+    const Key key{s.B, s.H, s.F, s.T, s.d, s.window, s.ref_frame, s.dtype, M};
     std::lock_guard<std::mutex> lock(g_cache_mu);
     auto it = g_cache.find(key);
     if (it != g_cache.end()) {
@@ -153,7 +165,7 @@ fsa_status cached_plan(const fsa_shape& s, const fsa_plan** out) {
         return FSA_OK;
     }
     fsa_plan* p = nullptr;
-    fsa_status st = fsa_plan_create(&s, &p);
+    fsa_status st = M > 0 ? fsa_plan_create_cross(&s, M, &p) : fsa_plan_create(&s, &p);
     if (st != FSA_OK) return st;
     try {
         g_cache.emplace(key, p);
@@ -186,55 +198,91 @@ extern "C" size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t wi
                                                 int32_t ref_frame, int32_t B, int32_t H,
                                                 int32_t d, int32_t dtype) {
     const fsa_plan* p = nullptr;
-    if (cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), &p) != FSA_OK) return 0;
+    if (cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), 0, &p) != FSA_OK)
+        return 0;
     return p->ws.total;
 }
+
+namespace {
+
+// bounds then forward with a cached plan; M > 0: cross-attention.
+fsa_status attend(const char* who, const void* Q, const void* K, const void* V, void* O,
+                  const fsa_shape& shape, int32_t M, float scale, int32_t mode, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    if (!Q || !K || !V || !O) {
+        set_error("%s: NULL Q, K, V or O", who);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!good_scale(scale)) {
+        set_error("%s: scale must be finite and > 0 (got %g)", who, double(scale));
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
+        mode != FSA_MODE_AUTO_FRAME) {
+        set_error("%s: unknown mode %d", who, mode);
+        return FSA_ERR_INVALID_ARG;
+    }
+    const fsa_plan* p = nullptr;
+    fsa_status st = cached_plan(shape, M, &p);
+    if (st != FSA_OK) return st;
+    if (!ws || ws_bytes < p->ws.total) {
+        set_error("%s: workspace of %zu bytes, %zu needed", who, ws ? ws_bytes : size_t(0),
+                  p->ws.total);
+        return FSA_ERR_WORKSPACE;
+    }
+    const size_t nb = tensor_bytes(*p), kb = kv_bytes(*p);
+    if (overlaps(O, nb, K, kb)) {
+        set_error("%s: O overlaps K", who);
+        return FSA_ERR_INVALID_ARG;
+    }
+    // Validate both calls before launching either.
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) {
+        set_error("%s: Q, K, V and O must be 16-byte aligned", who);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(ws, 256)) {
+        set_error("%s: workspace not 256-byte aligned", who);
+        return FSA_ERR_WORKSPACE;
+    }
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, V, kb) || overlaps(O, nb, ws, p->ws.total)) {
+        set_error("%s: O overlaps Q, V or the workspace", who);
+        return FSA_ERR_INVALID_ARG;
+    }
+    st = fsa_bounds(p, Q, K, ws, scale, stream);
+    if (st != FSA_OK) return st;
+    return fsa_forward(p, Q, K, V, O, ws, scale, mode, stream);
+}
+
+}  // namespace
 
 extern "C" fsa_status fsa_attention(const void* Q, const void* K, const void* V, void* O,
                                     int32_t F, int32_t T, int32_t window, int32_t ref_frame,
                                     float scale, int32_t B, int32_t H, int32_t d, int32_t dtype,
                                     int32_t mode, void* ws, size_t ws_bytes,
                                     hipStream_t stream) {
-    if (!Q || !K || !V || !O) {
-        set_error("fsa_attention: NULL Q, K, V or O");
-        return FSA_ERR_INVALID_ARG;
-    }
-    if (!good_scale(scale)) {
-        set_error("fsa_attention: scale must be finite and > 0 (got %g)", double(scale));
-        return FSA_ERR_INVALID_ARG;
-    }
-    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
-        mode != FSA_MODE_AUTO_FRAME) {
-        set_error("fsa_attention: unknown mode %d", mode);
-        return FSA_ERR_INVALID_ARG;
-    }
+    return attend("fsa_attention", Q, K, V, O, make_shape(F, T, window, ref_frame, B, H, d, dtype),
+                  0, scale, mode, ws, ws_bytes, stream);
+}
+
+extern "C" size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int32_t B,
+                                                      int32_t H, int32_t d, int32_t dtype) {
     const fsa_plan* p = nullptr;
-    fsa_status st = cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), &p);
-    if (st != FSA_OK) return st;
-    if (!ws || ws_bytes < p->ws.total) {
-        set_error("fsa_attention: workspace of %zu bytes, %zu needed", ws ? ws_bytes : size_t(0),
-                  p->ws.total);
-        return FSA_ERR_WORKSPACE;
+    if (M <= 0) {
+        set_error("fsa_cross_attention_workspace_bytes: M=%d must be positive", M);
+        return 0;
     }
-    const size_t nb = tensor_bytes(*p);
-    if (overlaps(O, nb, K, nb)) {
-        set_error("fsa_attention: O overlaps K");
+    if (cached_plan(make_shape(F, T, 0, 0, B, H, d, dtype), M, &p) != FSA_OK) return 0;
+    return p->ws.total;
+}
+
+extern "C" fsa_status fsa_cross_attention(const void* Q, const void* Kr, const void* Vr, void* O,
+                                          int32_t F, int32_t T, int32_t M, float scale, int32_t B,
+                                          int32_t H, int32_t d, int32_t dtype, int32_t mode,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (M <= 0) {
+        set_error("fsa_cross_attention: M=%d must be positive", M);
         return FSA_ERR_INVALID_ARG;
     }
-    // Validate both calls before launching either.
-    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) {
-        set_error("fsa_attention: Q, K, V and O must be 16-byte aligned");
-        return FSA_ERR_INVALID_ARG;
-    }
-    if (!aligned(ws, 256)) {
-        set_error("fsa_attention: workspace not 256-byte aligned");
-        return FSA_ERR_WORKSPACE;
-    }
-    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, V, nb) || overlaps(O, nb, ws, p->ws.total)) {
-        set_error("fsa_attention: O overlaps Q, V or the workspace");
-        return FSA_ERR_INVALID_ARG;
-    }
-    st = fsa_bounds(p, Q, K, ws, scale, stream);
-    if (st != FSA_OK) return st;
-    return fsa_forward(p, Q, K, V, O, ws, scale, mode, stream);
+    return attend("fsa_cross_attention", Q, Kr, Vr, O, make_shape(F, T, 0, 0, B, H, d, dtype), M,
+                  scale, mode, ws, ws_bytes, stream);
 }

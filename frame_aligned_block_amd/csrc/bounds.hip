@@ -9,9 +9,11 @@
 // for the online route.
 //
 // HBM-bound: K is read twice (mean, then the radii of the centred keys) and Q
-// once; nothing of the size of K is written. The centred keys themselves are
-// never stored: the forward pass scores K as given and moves each row's shift
-// by scale * q.mu instead. Every reduction is deterministic: sums in a fixed
+// once; nothing of the size of K is written. The key side is the chunk's own
+// frames (self-attention) or a separate set of M reference tokens that every
+// query attends to (cross-attention: one key frame, one radius per head). The
+// centred keys themselves are never stored: the forward pass scores K as given
+// and moves each row's shift by scale * q.mu instead. Every reduction is deterministic: sums in a fixed
 // order, maxima exact.
 #include <hip/hip_runtime.h>
 
@@ -39,25 +41,36 @@ __device__ __forceinline__ void store16(E* p, const Pack16<E>& r) {
     *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(r.v);
 }
 
-// Rows of one workgroup: part `part` of the frame grid, never crossing a frame.
+// Parts as the kernels read them (fsa::Parts without its host helpers).
+struct PartsArg {
+    int span, rows_per_part, per_frame, count;
+};
+
+PartsArg parts_arg(const fsa::Parts& g) { return {g.span, g.rows_per_part, g.per_frame, g.count()}; }
+
+// Rows of one workgroup: part `part` of one side, never crossing a frame.
 struct PartRows {
     int begin, end;
 };
 
-__device__ __forceinline__ PartRows part_rows(int part, int T, int rows_per_part, int ppf) {
-    const int frame = part / ppf, sub = part % ppf;
+__device__ __forceinline__ PartRows part_rows(int part, const PartsArg& g) {
+    const int frame = part / g.per_frame, sub = part % g.per_frame;
     PartRows r;
-    r.begin = frame * T + sub * rows_per_part;
-    r.end = min(frame * T + T, r.begin + rows_per_part);
+    r.begin = frame * g.span + sub * g.rows_per_part;
+    r.end = min(frame * g.span + g.span, r.begin + g.rows_per_part);
     return r;
 }
 
 // Pass 1: per-part column sums of K (for the mean) and row norms of Q.
-template <typename E, int D>
+// JOINT: the query and key sides share one part geometry (self-attention),
+// and each workgroup reads its rows of Q and K in the same loop. Otherwise
+// workgroup `part` reduces key part `part` and query part `part`, each where
+// it exists.
+template <typename E, int D, bool JOINT>
 __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
     const E* __restrict__ Q, const E* __restrict__ K, float* __restrict__ colsum,
-    float* __restrict__ qnorm, float* __restrict__ partqmax, int N, int T, int rows_per_part,
-    int ppf, int nparts) {
+    float* __restrict__ qnorm, float* __restrict__ partqmax, int N, int NK, PartsArg qp,
+    PartsArg kp) {
     constexpr int V = Pack16<E>::n;
     constexpr int LPR = D / V;        // lanes per row
     constexpr int RPI = 256 / LPR;    // rows per iteration
@@ -65,21 +78,20 @@ __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
     __shared__ float qred[RPI];
 
     const int part = blockIdx.x, bh = blockIdx.y;
-    const PartRows pr = part_rows(part, T, rows_per_part, ppf);
     const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
-    const size_t base = size_t(bh) * N * D;
+    const E* Qh = Q + size_t(bh) * N * D;
+    const E* Kh = K + size_t(bh) * NK * D;
+    const bool has_k = part < kp.count, has_q = part < qp.count;   // uniform
 
     float acc[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = 0.f;
     float qbest = 0.f;
-    for (int r = pr.begin + r0; r < pr.end; r += RPI) {
-        const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
-        const Pack16<E> q = load16(Q + base + size_t(r) * D + lane * V);
+    auto qrow = [&](int r) {
+        const Pack16<E> q = load16(Qh + size_t(r) * D + lane * V);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            acc[e] += float(k.v[e]);
             const float qe = float(q.v[e]);
             ss = fmaf(qe, qe, ss);
         }
@@ -88,57 +100,78 @@ __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
         const float qn = sqrtf(ss);
         qbest = fmaxf(qbest, qn);
         if (lane == 0) qnorm[size_t(bh) * N + r] = qn;
+    };
+    auto krow = [&](int r) {
+        const Pack16<E> k = load16(Kh + size_t(r) * D + lane * V);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] += float(k.v[e]);
+    };
+    if (JOINT) {
+        const PartRows pr = part_rows(part, qp);
+        for (int r = pr.begin + r0; r < pr.end; r += RPI) {
+            krow(r);
+            qrow(r);
+        }
+    } else {
+        if (has_k) {
+            const PartRows pr = part_rows(part, kp);
+            for (int r = pr.begin + r0; r < pr.end; r += RPI) krow(r);
+        }
+        if (has_q) {
+            const PartRows pr = part_rows(part, qp);
+            for (int r = pr.begin + r0; r < pr.end; r += RPI) qrow(r);
+        }
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) red[r0][lane * V + e] = acc[e];
     if (lane == 0) qred[r0] = qbest;
     __syncthreads();
-    if (threadIdx.x < D) {
+    if (threadIdx.x < D && has_k) {
         float s = 0.f;
         for (int i = 0; i < RPI; ++i) s += red[i][threadIdx.x];
-        colsum[(size_t(bh) * nparts + part) * D + threadIdx.x] = s;
+        colsum[(size_t(bh) * kp.count + part) * D + threadIdx.x] = s;
     }
-    if (threadIdx.x == D) {
+    if (threadIdx.x == D && has_q) {
         float b = 0.f;
         for (int i = 0; i < RPI; ++i) b = fmaxf(b, qred[i]);
-        partqmax[size_t(bh) * nparts + part] = b;
+        partqmax[size_t(bh) * qp.count + part] = b;
     }
 }
 
 // Pass 2: the key mean of each (batch, head), summing the parts in order.
 template <int D>
 __global__ __launch_bounds__(256) void bounds_mean(const float* __restrict__ colsum,
-                                                   float* __restrict__ mu, int N, int nparts) {
+                                                   float* __restrict__ mu, int NK, int nparts) {
     const int bh = blockIdx.x, t = threadIdx.x;
     if (t >= D) return;
     float s = 0.f;
     const float* col = colsum + size_t(bh) * nparts * D + t;
 #pragma unroll 16       // loads issue ahead; the additions keep their order
     for (int p = 0; p < nparts; ++p) s += col[size_t(p) * D];
-    mu[size_t(bh) * D + t] = s / float(N);
+    mu[size_t(bh) * D + t] = s / float(NK);
 }
 
 // Pass 3: the part's largest ||k_j - mu||, in fp32 from the keys as given.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bounds_radius(
-    const E* __restrict__ K, const float* __restrict__ mu, float* __restrict__ partmax, int N,
-    int T, int rows_per_part, int ppf, int nparts) {
+    const E* __restrict__ K, const float* __restrict__ mu, float* __restrict__ partmax, int NK,
+    PartsArg kp) {
     constexpr int V = Pack16<E>::n;
     constexpr int LPR = D / V;
     constexpr int RPI = 256 / LPR;
     __shared__ float red[RPI];
 
     const int part = blockIdx.x, bh = blockIdx.y;
-    const PartRows pr = part_rows(part, T, rows_per_part, ppf);
+    const PartRows pr = part_rows(part, kp);
     const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
-    const size_t base = size_t(bh) * N * D;
+    const E* Kh = K + size_t(bh) * NK * D;
 
     float m[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) m[e] = mu[size_t(bh) * D + lane * V + e];
     float best = 0.f;
     for (int r = pr.begin + r0; r < pr.end; r += RPI) {
-        const Pack16<E> k = load16(K + base + size_t(r) * D + lane * V);
+        const Pack16<E> k = load16(Kh + size_t(r) * D + lane * V);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -154,11 +187,11 @@ __global__ __launch_bounds__(256) void bounds_radius(
     if (threadIdx.x == 0) {
         float b = 0.f;
         for (int i = 0; i < RPI; ++i) b = fmaxf(b, red[i]);
-        partmax[size_t(bh) * nparts + part] = b;
+        partmax[size_t(bh) * kp.count + part] = b;
     }
 }
 
-// Pass 4, per (batch, head): per-frame key radius, per-slice radius, the
+// Pass 4, per (batch, head): per-key-frame radius, per-slice radius, the
 // largest row bound scale * ||q_i|| * R_S(f(i)) and the eligibility flag.
 // Maxima are exact, so any reduction order gives the same bits. The largest
 // row bound of frame f is (scale * max ||q_i||) * R_S(f): rounding is monotone.
@@ -166,20 +199,23 @@ __global__ __launch_bounds__(256) void bounds_finalize(
     const float* __restrict__ partqmax, const float* __restrict__ partmax,
     float* __restrict__ rframe, float* __restrict__ rslice, float* __restrict__ stat,
     uint8_t* __restrict__ elig, float* __restrict__ statf, uint8_t* __restrict__ eligf, int F,
-    int ppf, float scale, const FrameTable tab) {
+    int KF, PartsArg qp, PartsArg kp, float scale, const FrameTable tab) {
     __shared__ float rf[FSA_MAX_FRAMES + 1];
     __shared__ float qm[FSA_MAX_FRAMES + 1];
     __shared__ float sb[FSA_MAX_FRAMES + 1];
     const int bh = blockIdx.x;
-    for (int g = threadIdx.x; g < F; g += blockDim.x) {
-        float b = 0.f, q = 0.f;
-        for (int s = 0; s < ppf; ++s) {
-            b = fmaxf(b, partmax[size_t(bh) * F * ppf + g * ppf + s]);
-            q = fmaxf(q, partqmax[size_t(bh) * F * ppf + g * ppf + s]);
-        }
+    for (int g = threadIdx.x; g < KF; g += blockDim.x) {
+        float b = 0.f;
+        for (int s = 0; s < kp.per_frame; ++s)
+            b = fmaxf(b, partmax[size_t(bh) * kp.count + g * kp.per_frame + s]);
         rf[g] = b;
-        qm[g] = q;
-        rframe[size_t(bh) * F + g] = b;
+        rframe[size_t(bh) * KF + g] = b;
+    }
+    for (int f = threadIdx.x; f < F; f += blockDim.x) {
+        float q = 0.f;
+        for (int s = 0; s < qp.per_frame; ++s)
+            q = fmaxf(q, partqmax[size_t(bh) * qp.count + f * qp.per_frame + s]);
+        qm[f] = q;
     }
     __syncthreads();
     for (int f = threadIdx.x; f < F; f += blockDim.x) {
@@ -207,8 +243,8 @@ template <typename E, int D>
 fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* wsv, float scale,
                       hipStream_t stream) {
     const fsa_shape& s = p.shape;
-    const int N = s.F * s.T, BH = s.B * s.H;
-    const int ppf = p.bounds.parts_per_frame, nparts = s.F * ppf;
+    const int N = s.F * s.T, NK = int(p.key_tokens()), BH = s.B * s.H;
+    const PartsArg qp = parts_arg(p.bounds.q), kp = parts_arg(p.bounds.k);
     char* ws = static_cast<char*>(wsv);
     const E* Q = static_cast<const E*>(Qv);
     const E* K = static_cast<const E*>(Kv);
@@ -217,19 +253,25 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
     float* colsum = reinterpret_cast<float*>(ws + p.bounds.colsum);
     float* partmax = reinterpret_cast<float*>(ws + p.bounds.partmax);
     float* partqmax = reinterpret_cast<float*>(ws + p.bounds.partqmax);
-    const dim3 grid(nparts, BH);
-    hipLaunchKernelGGL((bounds_colsum_qnorm<E, D>), grid, dim3(256), 0, stream, Q, K, colsum, qn,
-                       partqmax, N, s.T, p.bounds.rows_per_part, ppf, nparts);
-    hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, N, nparts);
-    hipLaunchKernelGGL((bounds_radius<E, D>), grid, dim3(256), 0, stream, K, mu, partmax, N, s.T,
-                       p.bounds.rows_per_part, ppf, nparts);
+    const bool joint = !p.cross;      // one part geometry for both sides
+    const dim3 grid1(max(qp.count, kp.count), BH);
+    if (joint)
+        hipLaunchKernelGGL((bounds_colsum_qnorm<E, D, true>), grid1, dim3(256), 0, stream, Q, K,
+                           colsum, qn, partqmax, N, NK, qp, kp);
+    else
+        hipLaunchKernelGGL((bounds_colsum_qnorm<E, D, false>), grid1, dim3(256), 0, stream, Q, K,
+                           colsum, qn, partqmax, N, NK, qp, kp);
+    hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, NK, kp.count);
+    hipLaunchKernelGGL((bounds_radius<E, D>), dim3(kp.count, BH), dim3(256), 0, stream, K, mu,
+                       partmax, NK, kp);
     hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, partqmax, partmax,
                        reinterpret_cast<float*>(ws + p.ws.rframe),
                        reinterpret_cast<float*>(ws + p.ws.rslice),
                        reinterpret_cast<float*>(ws + p.ws.stat),
                        reinterpret_cast<uint8_t*>(ws + p.ws.elig),
                        reinterpret_cast<float*>(ws + p.ws.statf),
-                       reinterpret_cast<uint8_t*>(ws + p.ws.eligf), s.F, ppf, scale, p.table);
+                       reinterpret_cast<uint8_t*>(ws + p.ws.eligf), s.F, p.key_frames, qp, kp,
+                       scale, p.table);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));

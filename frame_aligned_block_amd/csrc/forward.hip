@@ -64,6 +64,8 @@ struct FwdArgs {
     const uint8_t* eligf;       // per (batch, head, frame)
     float c;                    // scale * log2(e)
     int32_t N, T, F, BH;
+    int32_t NK;                 // key (and value) tokens per (batch, head)
+    int32_t KT;                 // tokens per key frame: the run table's unit
     int32_t units_per_frame;    // row units of 16*G rows per frame
     int32_t groups_per_frame;   // workgroups per (batch*head, frame)
     int32_t nwg;                // total workgroups
@@ -88,13 +90,15 @@ struct Slice {
     __device__ __forceinline__ int key(int x) const { return x < n0 ? s0 + x : s1 + (x - n0); }
 };
 
-__device__ __forceinline__ Slice slice_of(const FrameTable& t, int f, int T) {
+// Query frame f's key slice, in tokens: the run table counts key frames of KT
+// tokens (the chunk's frames, or the whole reference set for cross-attention).
+__device__ __forceinline__ Slice slice_of(const FrameTable& t, int f, int KT) {
     const uint32_t run = t.runs[f];
     Slice s;
-    s.s0 = int(run & 0xff) * T;
-    s.n0 = int((run >> 8) & 0xff) * T;
-    s.s1 = int((run >> 16) & 0xff) * T;
-    s.total = s.n0 + int(run >> 24) * T;
+    s.s0 = int(run & 0xff) * KT;
+    s.n0 = int((run >> 8) & 0xff) * KT;
+    s.s1 = int((run >> 16) & 0xff) * KT;
+    s.total = s.n0 + int(run >> 24) * KT;
     return s;
 }
 
@@ -608,13 +612,13 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const int f = frame_at(p.tab, t1 % p.F);
     const int bh = t1 / p.F;
     const int T = p.T;
-    const Slice sl = slice_of(p.tab, f, T);
+    const Slice sl = slice_of(p.tab, f, p.KT);
 
-    const size_t base = size_t(bh) * p.N * D;
+    const size_t base = size_t(bh) * p.N * D, kbase = size_t(bh) * p.NK * D;
     const __bf16* Qh = static_cast<const __bf16*>(p.Q) + base;
     const bool fixed = use_fixed(p, bh, f);              // uniform per workgroup
-    const __bf16* Kh = static_cast<const __bf16*>(p.K) + base;
-    const __bf16* Vh = static_cast<const __bf16*>(p.V) + base;
+    const __bf16* Kh = static_cast<const __bf16*>(p.K) + kbase;
+    const __bf16* Vh = static_cast<const __bf16*>(p.V) + kbase;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
 
     // A wave owns granules unit*G .. unit*G+G-1 of frame f. Granules past the
@@ -699,12 +703,12 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     if (gid >= int64_t(p.BH) * p.N) return;
     const int bh = int(gid / p.N), i = int(gid % p.N);
     const int T = p.T, f = i / T;
-    const Slice sl = slice_of(p.tab, f, T);
-    const size_t base = size_t(bh) * p.N * D;
+    const Slice sl = slice_of(p.tab, f, p.KT);
+    const size_t base = size_t(bh) * p.N * D, kbase = size_t(bh) * p.NK * D;
     const bool fixed = use_fixed(p, bh, f);
     const float* Qh = static_cast<const float*>(p.Q) + base;
-    const float* Kh = static_cast<const float*>(p.K) + base;
-    const float* Vh = static_cast<const float*>(p.V) + base;
+    const float* Kh = static_cast<const float*>(p.K) + kbase;
+    const float* Vh = static_cast<const float*>(p.V) + kbase;
     float* Oh = static_cast<float*>(p.O) + base;
     const float c = p.c;
 
@@ -772,6 +776,8 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
     a.eligf = reinterpret_cast<const uint8_t*>(ws + p.ws.eligf);
     a.c = scale * kLog2e;
     a.N = s.F * s.T;
+    a.NK = int32_t(p.key_tokens());
+    a.KT = p.key_span;
     a.T = s.T;
     a.F = s.F;
     a.BH = s.B * s.H;

@@ -13,9 +13,11 @@ namespace fsa {
 // Per-frame key runs as the kernels read them (kernel arguments, so they land
 // in scalar registers / the constant cache: the gfx950 counterpart of feeding
 // a small table to the kernel ahead of its grid, "Unchaining the Softmax" ¶2).
-// runs[f] packs, in frame units, the up to two contiguous key ranges of frame
-// f's slice, in ascending key order:
+// runs[f] packs, in key-frame units, the up to two contiguous key ranges of
+// query frame f's slice, in ascending key order:
 //   bits 0-7 start0, 8-15 len0, 16-23 start1, 24-31 len1   (len1 may be 0).
+// A key frame is T tokens of the chunk itself (self-attention) or the whole
+// set of M reference tokens (cross-attention: every frame's slice is {0, 1}).
 // order[] lists frames heaviest slice first (4 frame ids per word), which is
 // the order workgroups are handed out in.
 struct FrameTable {
@@ -31,12 +33,22 @@ struct FrameTable {
 constexpr int kWaves = FSA_WAVES;
 constexpr int kThreads = 64 * kWaves;
 
+// Rows of one side (queries or keys) cut into parts of at most 256 rows
+// that never straddle a frame of that side.
+struct Parts {
+    int32_t span;             // rows per frame of this side
+    int32_t frames;           // frames of this side
+    int32_t rows_per_part;    // rows one bounds workgroup reduces
+    int32_t per_frame;        // ceil(span / rows_per_part)
+    int32_t count() const { return frames * per_frame; }
+};
+
 struct BoundsGeometry {
-    int32_t rows_per_part;    // key/query rows one bounds workgroup reduces
-    int32_t parts_per_frame;  // ceil(T / rows_per_part)
-    size_t colsum;            // private ws offsets: float [BH][F*ppf][d]
-    size_t partmax;           // float [BH][F*ppf]: max ||k_j - mu|| per part
-    size_t partqmax;          // float [BH][F*ppf]: max ||q_i|| per part
+    Parts q;                  // query rows: F frames of T
+    Parts k;                  // key rows: the key frames (F of T, or one of M)
+    size_t colsum;            // private ws offsets: float [BH][k parts][d]
+    size_t partmax;           // float [BH][k parts]: max ||k_j - mu|| per part
+    size_t partqmax;          // float [BH][q parts]: max ||q_i|| per part
 };
 
 struct ForwardGeometry {
@@ -50,6 +62,12 @@ struct ForwardGeometry {
 
 struct fsa_plan {
     fsa_shape shape;                 // bq, bk resolved
+    // Key side. Self-attention: the chunk's own F frames of T tokens.
+    // Cross-attention: one key frame of M reference tokens that every query
+    // frame attends to. The run table counts in key frames of key_span tokens.
+    bool cross = false;
+    int32_t key_frames = 0, key_span = 0;
+    int64_t key_tokens() const { return int64_t(key_frames) * key_span; }
     int32_t n_qblocks = 0, n_kblocks = 0;
     std::vector<int32_t> row_ptr, col_idx, qframe, runs;   // runs: 4 per q-block
     std::vector<int32_t> slice_size;                       // |S(f)| per frame

@@ -43,71 +43,104 @@ int32_t pick_bk(int32_t T) {
     return 16;
 }
 
-}  // namespace
+// Parts of at most 256 rows over `frames` frames of `span` rows each.
+fsa::Parts make_parts(int32_t frames, int32_t span) {
+    fsa::Parts g;
+    g.span = span;
+    g.frames = frames;
+    const int32_t parts = (span + 255) / 256;
+    g.rows_per_part = (span + parts - 1) / parts;
+    g.per_frame = (span + g.rows_per_part - 1) / g.rows_per_part;
+    return g;
+}
 
-extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
+// The builder behind fsa_plan_create (M = 0: self-attention over the chunk's
+// own frames) and fsa_plan_create_cross (M reference tokens, one key frame).
+fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const char* who) {
     using namespace fsa;
     if (!s_in || !out) {
-        set_error("fsa_plan_create: NULL argument");
+        set_error("%s: NULL argument", who);
         return FSA_ERR_INVALID_ARG;
     }
     *out = nullptr;
+    const bool cross = M != 0;
     fsa_shape s = *s_in;
     if (s.B < 1 || s.H < 1 || s.F < 1 || s.T < 1 || s.window < 0 ||
         s.ref_frame < 0 || s.ref_frame >= s.F || s.bq < 0 || s.bk < 0 ||
         (s.dtype != FSA_BF16 && s.dtype != FSA_F32)) {
-        set_error("fsa_plan_create: invalid shape (B=%d H=%d F=%d T=%d window=%d ref=%d bq=%d bk=%d dtype=%d)",
-                  s.B, s.H, s.F, s.T, s.window, s.ref_frame, s.bq, s.bk, s.dtype);
+        set_error("%s: invalid shape (B=%d H=%d F=%d T=%d window=%d ref=%d bq=%d bk=%d dtype=%d)",
+                  who, s.B, s.H, s.F, s.T, s.window, s.ref_frame, s.bq, s.bk, s.dtype);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (cross && (M < 0 || s.window != 0 || s.ref_frame != 0)) {
+        set_error("%s: M=%d must be positive and window=%d, ref_frame=%d both 0 (every query "
+                  "attends to the whole reference set)", who, M, s.window, s.ref_frame);
         return FSA_ERR_INVALID_ARG;
     }
     if (s.T % 16 != 0) {
-        set_error("fsa_plan_create: T=%d is not a multiple of 16; frame-aligned blocks need 16 | T", s.T);
+        set_error("%s: T=%d is not a multiple of 16; frame-aligned blocks need 16 | T", who, s.T);
+        return FSA_ERR_UNSUPPORTED;
+    }
+    if (cross && M % 16 != 0) {
+        set_error("%s: M=%d is not a multiple of 16; key blocks need 16 | M", who, M);
         return FSA_ERR_UNSUPPORTED;
     }
     if (s.d != 64 && s.d != 128) {
-        set_error("fsa_plan_create: head width d=%d unsupported (64 or 128)", s.d);
+        set_error("%s: head width d=%d unsupported (64 or 128)", who, s.d);
         return FSA_ERR_UNSUPPORTED;
     }
     if (s.F > FSA_MAX_FRAMES) {
-        set_error("fsa_plan_create: F=%d above the limit %d", s.F, FSA_MAX_FRAMES);
+        set_error("%s: F=%d above the limit %d", who, s.F, FSA_MAX_FRAMES);
         return FSA_ERR_UNSUPPORTED;
     }
     const int64_t N = int64_t(s.F) * s.T;
-    if (int64_t(s.B) * s.H * N * s.d > 0x7fffffffLL) {
-        set_error("fsa_plan_create: B*H*N*d above 2^31-1 elements");
+    const int32_t KF = cross ? 1 : s.F, KT = cross ? M : s.T;
+    const int64_t NK = int64_t(KF) * KT;
+    if (int64_t(s.B) * s.H * N * s.d > 0x7fffffffLL ||
+        int64_t(s.B) * s.H * NK * s.d > 0x7fffffffLL) {
+        set_error("%s: B*H*N*d or B*H*(key tokens)*d above 2^31-1 elements", who);
         return FSA_ERR_UNSUPPORTED;
     }
-    for (int32_t b : {s.bq, s.bk}) {
-        if (b != 0 && (b % 16 != 0 || s.T % b != 0)) {
-            set_error("fsa_plan_create: block size %d is not a multiple of 16 dividing T=%d", b, s.T);
-            return FSA_ERR_INVALID_ARG;
-        }
+    if (s.bq != 0 && (s.bq % 16 != 0 || s.T % s.bq != 0)) {
+        set_error("%s: block size %d is not a multiple of 16 dividing T=%d", who, s.bq, s.T);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (s.bk != 0 && (s.bk % 16 != 0 || KT % s.bk != 0)) {
+        set_error("%s: block size %d is not a multiple of 16 dividing %s=%d", who, s.bk,
+                  cross ? "M" : "T", KT);
+        return FSA_ERR_INVALID_ARG;
     }
 
     fsa_plan* p = new (std::nothrow) fsa_plan();
     if (!p) {
-        set_error("fsa_plan_create: out of host memory");
+        set_error("%s: out of host memory", who);
         return FSA_ERR_NOMEM;
     }
     try {
         if (s.bq == 0) s.bq = pick_bq(s.T);
-        if (s.bk == 0) s.bk = pick_bk(s.T);
+        if (s.bk == 0) s.bk = pick_bk(KT);
         p->shape = s;
+        p->cross = cross;
+        p->key_frames = KF;
+        p->key_span = KT;
 
-        // ---- slices and the per-frame run table
+        // ---- slices and the per-frame run table (in key frames)
         p->slice_size.assign(s.F, 0);
         std::vector<std::pair<int32_t, int32_t>> weight;   // (-|S|, f)
         for (int32_t f = 0; f < s.F; ++f) {
-            int32_t lo = std::max(0, f - s.window), hi = std::min(s.F - 1, f + s.window);
-            // runs in ascending frame order: the window, and the reference frame
-            // when it lies outside the window (merged if adjacent).
-            int32_t a0 = lo, l0 = hi - lo + 1, a1 = 0, l1 = 0;
-            if (s.ref_frame < lo) {
-                if (s.ref_frame == lo - 1) { a0 = s.ref_frame; l0 += 1; }
-                else { a1 = a0; l1 = l0; a0 = s.ref_frame; l0 = 1; }
-            } else if (s.ref_frame > hi) {
-                if (s.ref_frame == hi + 1) { l0 += 1; }
-                else { a1 = s.ref_frame; l1 = 1; }
+            int32_t a0 = 0, l0 = 1, a1 = 0, l1 = 0;
+            if (!cross) {
+                int32_t lo = std::max(0, f - s.window), hi = std::min(s.F - 1, f + s.window);
+                // runs in ascending frame order: the window, and the reference
+                // frame when it lies outside the window (merged if adjacent).
+                a0 = lo; l0 = hi - lo + 1;
+                if (s.ref_frame < lo) {
+                    if (s.ref_frame == lo - 1) { a0 = s.ref_frame; l0 += 1; }
+                    else { a1 = a0; l1 = l0; a0 = s.ref_frame; l0 = 1; }
+                } else if (s.ref_frame > hi) {
+                    if (s.ref_frame == hi + 1) { l0 += 1; }
+                    else { a1 = s.ref_frame; l1 = 1; }
+                }
             }
             p->table.runs[f] = uint32_t(a0) | uint32_t(l0) << 8 | uint32_t(a1) << 16 |
                                uint32_t(l1) << 24;
@@ -121,7 +154,7 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
 
         // ---- CSR tile list, built from the slice definition tile by tile
         p->n_qblocks = int32_t(N / s.bq);
-        p->n_kblocks = int32_t(N / s.bk);
+        p->n_kblocks = int32_t(NK / s.bk);
         p->row_ptr.reserve(p->n_qblocks + 1);
         p->row_ptr.push_back(0);
         p->qframe.reserve(p->n_qblocks);
@@ -130,14 +163,14 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
             const int32_t f = int32_t(int64_t(qb) * s.bq / s.T);
             int32_t nrun = 0, r[4] = {0, 0, 0, 0};
             for (int32_t kb = 0; kb < p->n_kblocks; ++kb) {
-                const int32_t g = int32_t(int64_t(kb) * s.bk / s.T);
-                if (!in_slice(s.F, s.window, s.ref_frame, f, g)) continue;
+                const int32_t g = int32_t(int64_t(kb) * s.bk / KT);
+                if (!cross && !in_slice(s.F, s.window, s.ref_frame, f, g)) continue;
                 p->col_idx.push_back(kb);
                 const int32_t a = kb * s.bk, e = a + s.bk;
                 if (nrun > 0 && r[2 * (nrun - 1) + 1] == a) r[2 * (nrun - 1) + 1] = e;
                 else {
                     if (nrun == 2) {   // cannot happen for window U {ref}
-                        set_error("fsa_plan_create: internal error, more than two key runs");
+                        set_error("%s: internal error, more than two key runs", who);
                         delete p;
                         return FSA_ERR_INVALID_ARG;
                     }
@@ -149,20 +182,19 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
             for (int32_t i = 0; i < 4; ++i) p->runs.push_back(r[i]);
             // The kernels read the per-frame table; it must agree with the list.
             const uint32_t t = p->table.runs[f];
-            const int32_t T = s.T;
-            const int32_t e0 = int32_t(t & 0xff) * T, e1 = e0 + int32_t((t >> 8) & 0xff) * T;
-            const int32_t e2 = int32_t((t >> 16) & 0xff) * T, e3 = e2 + int32_t(t >> 24) * T;
+            const int32_t e0 = int32_t(t & 0xff) * KT, e1 = e0 + int32_t((t >> 8) & 0xff) * KT;
+            const int32_t e2 = int32_t((t >> 16) & 0xff) * KT, e3 = e2 + int32_t(t >> 24) * KT;
             const bool ok = r[0] == e0 && r[1] == e1 &&
                             ((t >> 24) == 0 ? (r[2] == 0 && r[3] == 0) : (r[2] == e2 && r[3] == e3));
             if (!ok) {
-                set_error("fsa_plan_create: internal error, run table disagrees with tile list");
+                set_error("%s: internal error, run table disagrees with tile list", who);
                 delete p;
                 return FSA_ERR_INVALID_ARG;
             }
         }
         int64_t total = 0;
         for (int32_t f = 0; f < s.F; ++f) total += p->slice_size[f];
-        p->valid_pairs = total * int64_t(s.T) * s.T;
+        p->valid_pairs = total * int64_t(s.T) * KT;
 
         // ---- forward geometry: each wave takes `granules` consecutive 16-row
         // granules of one frame; a frame's last unit may hold fewer.
@@ -172,10 +204,9 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         p->forward.groups_per_frame = (p->forward.units_per_frame + kWaves - 1) / kWaves;
         p->forward.workgroups = int64_t(s.B) * s.H * s.F * p->forward.groups_per_frame;
 
-        // ---- bounds geometry: parts never straddle a frame
-        const int32_t parts = (s.T + 255) / 256;
-        p->bounds.rows_per_part = (s.T + parts - 1) / parts;
-        p->bounds.parts_per_frame = (s.T + p->bounds.rows_per_part - 1) / p->bounds.rows_per_part;
+        // ---- bounds geometry: parts never straddle a frame of their side
+        p->bounds.q = make_parts(s.F, s.T);
+        p->bounds.k = make_parts(KF, KT);
 
         // ---- workspace layout
         const size_t BH = size_t(s.B) * s.H;
@@ -183,24 +214,39 @@ extern "C" fsa_status fsa_plan_create(const fsa_shape* s_in, fsa_plan** out) {
         fsa_ws_layout& w = p->ws;
         w.mu = off;      off = align_up(off + BH * s.d * 4);
         w.qnorm = off;   off = align_up(off + BH * N * 4);
-        w.rframe = off;  off = align_up(off + BH * s.F * 4);
+        w.rframe = off;  off = align_up(off + BH * KF * 4);
         w.rslice = off;  off = align_up(off + BH * s.F * 4);
         w.stat = off;    off = align_up(off + BH * 4);
         w.elig = off;    off = align_up(off + BH);
         w.statf = off;   off = align_up(off + BH * s.F * 4);
         w.eligf = off;   off = align_up(off + BH * s.F);
-        const size_t nparts = size_t(s.F) * p->bounds.parts_per_frame;
-        p->bounds.colsum = off;  off = align_up(off + BH * nparts * s.d * 4);
-        p->bounds.partmax = off; off = align_up(off + BH * nparts * 4);
-        p->bounds.partqmax = off; off = align_up(off + BH * nparts * 4);
+        const size_t nkparts = size_t(p->bounds.k.count()), nqparts = size_t(p->bounds.q.count());
+        p->bounds.colsum = off;  off = align_up(off + BH * nkparts * s.d * 4);
+        p->bounds.partmax = off; off = align_up(off + BH * nkparts * 4);
+        p->bounds.partqmax = off; off = align_up(off + BH * nqparts * 4);
         w.total = off;
     } catch (const std::bad_alloc&) {
         delete p;
-        set_error("fsa_plan_create: out of host memory");
+        set_error("%s: out of host memory", who);
         return FSA_ERR_NOMEM;
     }
     *out = p;
     return FSA_OK;
+}
+
+}  // namespace
+
+extern "C" fsa_status fsa_plan_create(const fsa_shape* shape, fsa_plan** out) {
+    return create_plan(shape, 0, out, "fsa_plan_create");
+}
+
+extern "C" fsa_status fsa_plan_create_cross(const fsa_shape* shape, int32_t M, fsa_plan** out) {
+    if (M <= 0) {
+        fsa::set_error("fsa_plan_create_cross: M=%d must be positive", M);
+        if (out) *out = nullptr;
+        return FSA_ERR_INVALID_ARG;
+    }
+    return create_plan(shape, M, out, "fsa_plan_create_cross");
 }
 
 extern "C" void fsa_plan_destroy(fsa_plan* plan) { delete plan; }
@@ -232,6 +278,10 @@ extern "C" fsa_status fsa_plan_export(const fsa_plan* plan, int32_t* row_ptr, in
 
 extern "C" int64_t fsa_plan_valid_pairs(const fsa_plan* plan) {
     return plan ? plan->valid_pairs : -1;
+}
+
+extern "C" int64_t fsa_plan_key_tokens(const fsa_plan* plan) {
+    return plan ? plan->key_tokens() : -1;
 }
 
 extern "C" size_t fsa_workspace_bytes(const fsa_plan* plan) {

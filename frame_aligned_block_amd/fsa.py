@@ -43,10 +43,11 @@ FSA_MAX_FRAMES = 255
 
 # Every symbol include/fsa.h declares.
 EXPORTS = (
-    "fsa_plan_create", "fsa_plan_destroy", "fsa_plan_shape", "fsa_plan_export",
-    "fsa_plan_valid_pairs", "fsa_workspace_bytes", "fsa_workspace_layout",
-    "fsa_bounds", "fsa_forward", "fsa_copy_eligibility", "fsa_attention",
-    "fsa_attention_workspace_bytes",
+    "fsa_plan_create", "fsa_plan_create_cross", "fsa_plan_destroy", "fsa_plan_shape",
+    "fsa_plan_export", "fsa_plan_valid_pairs", "fsa_plan_key_tokens", "fsa_workspace_bytes",
+    "fsa_workspace_layout", "fsa_bounds", "fsa_forward", "fsa_copy_eligibility",
+    "fsa_attention", "fsa_attention_workspace_bytes", "fsa_cross_attention",
+    "fsa_cross_attention_workspace_bytes",
     "fsa_cache_clear", "fsa_status_string", "fsa_last_error",
 )
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
     P = c_void_p
     L.fsa_plan_create.argtypes = [POINTER(fsa_shape), POINTER(P)]
     L.fsa_plan_create.restype = c_int32
+    L.fsa_plan_create_cross.argtypes = [POINTER(fsa_shape), c_int32, POINTER(P)]
+    L.fsa_plan_create_cross.restype = c_int32
     L.fsa_plan_destroy.argtypes = [P]
     L.fsa_plan_destroy.restype = None
     L.fsa_plan_shape.argtypes = [P, POINTER(fsa_shape)]
@@ -90,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.fsa_plan_export.restype = c_int32
     L.fsa_plan_valid_pairs.argtypes = [P]
     L.fsa_plan_valid_pairs.restype = c_int64
+    L.fsa_plan_key_tokens.argtypes = [P]
+    L.fsa_plan_key_tokens.restype = c_int64
     L.fsa_workspace_bytes.argtypes = [P]
     L.fsa_workspace_bytes.restype = c_size_t
     L.fsa_workspace_layout.argtypes = [P, POINTER(fsa_ws_layout)]
@@ -105,6 +110,11 @@ def lib() -> ctypes.CDLL:
     L.fsa_attention.restype = c_int32
     L.fsa_attention_workspace_bytes.argtypes = [c_int32] * 8
     L.fsa_attention_workspace_bytes.restype = c_size_t
+    L.fsa_cross_attention.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, c_float, c_int32,
+                                      c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]
+    L.fsa_cross_attention.restype = c_int32
+    L.fsa_cross_attention_workspace_bytes.argtypes = [c_int32] * 7
+    L.fsa_cross_attention_workspace_bytes.restype = c_size_t
     L.fsa_cache_clear.argtypes = []
     L.fsa_cache_clear.restype = None
     L.fsa_status_string.argtypes = [c_int32]
@@ -156,10 +166,12 @@ def _stream(stream) -> int | None:
 # ------------------------------------------------------------------ plan
 
 class Plan:
-    """Owns an fsa_plan handle (host memory)."""
+    """Owns an fsa_plan handle (host memory). M: reference tokens of a cross
+    plan, 0 for self-attention."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, M: int = 0):
         self.handle = handle
+        self.M = M
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:
@@ -179,6 +191,12 @@ def fsa_plan_create(shape: fsa_shape) -> Plan:
     h = c_void_p()
     _check(lib().fsa_plan_create(ctypes.byref(shape), ctypes.byref(h)))
     return Plan(h.value)
+
+
+def fsa_plan_create_cross(shape: fsa_shape, M: int) -> Plan:
+    h = c_void_p()
+    _check(lib().fsa_plan_create_cross(ctypes.byref(shape), int(M), ctypes.byref(h)))
+    return Plan(h.value, int(M))
 
 
 def fsa_plan_destroy(plan: Plan) -> None:
@@ -211,6 +229,10 @@ def fsa_plan_export(plan: Plan) -> dict:
 
 def fsa_plan_valid_pairs(plan: Plan) -> int:
     return int(lib().fsa_plan_valid_pairs(plan))
+
+
+def fsa_plan_key_tokens(plan: Plan) -> int:
+    return int(lib().fsa_plan_key_tokens(plan))
 
 
 def fsa_workspace_bytes(plan: Plan) -> int:
@@ -260,6 +282,21 @@ def fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, dtype) -> in
     return n
 
 
+def fsa_cross_attention(Q, Kr, Vr, O, F, T, M, scale, B, H, d, dtype, mode, ws, ws_bytes,
+                        stream=None) -> None:
+    mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().fsa_cross_attention(_ptr(Q), _ptr(Kr), _ptr(Vr), _ptr(O), F, T, M, float(scale),
+                                     B, H, d, dtype, mode, _ptr(ws), int(ws_bytes),
+                                     _stream(stream)))
+
+
+def fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, dtype) -> int:
+    n = int(lib().fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, dtype))
+    if n == 0:
+        raise FsaError(FSA_ERR_INVALID_ARG, fsa_last_error())
+    return n
+
+
 def fsa_cache_clear() -> None:
     lib().fsa_cache_clear()
 
@@ -302,12 +339,42 @@ def attention(q, k, v, F: int, T: int, window: int, ref_frame: int, scale: float
     return out
 
 
+def cross_attention(q, kr, vr, F: int, T: int, scale: float | None = None, mode="auto",
+                    out=None, ws=None):
+    """O [B, H, F*T, d]: every query row of q attends to all M reference
+    tokens of kr, vr [B, H, M, d] (CUDA tensors). Calls fsa_cross_attention on
+    torch's current stream; allocates O and the workspace with torch unless
+    given."""
+    import torch
+    B, H, N, d = q.shape
+    M = kr.shape[2]
+    if N != F * T:
+        raise ValueError(f"N={N} != F*T={F * T}")
+    for t, shp in ((q, q.shape), (kr, (B, H, M, d)), (vr, (B, H, M, d))):
+        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shp) \
+                or t.dtype != q.dtype:
+            raise ValueError("q [B,H,F*T,d], kr and vr [B,H,M,d] must be contiguous CUDA "
+                             "tensors of one dtype")
+    if scale is None:
+        scale = d ** -0.5
+    code = dtype_code(q)
+    need = fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, code)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    fsa_cross_attention(q, kr, vr, out, F, T, M, scale, B, H, d, code, mode, ws,
+                        ws.numel() * ws.element_size())
+    return out
+
+
 def workspace_views(plan: Plan, ws):
     """Typed torch views of the bound products inside a workspace tensor."""
     import torch
     s = fsa_plan_shape(plan)
     lay = fsa_workspace_layout(plan)
     BH, N = s.B * s.H, s.F * s.T
+    KF = 1 if plan.M else s.F             # a cross plan has one key frame
 
     def view(off, n, dt, sz, shape):
         return ws[off:off + n * sz].view(dt).view(*shape)
@@ -315,7 +382,7 @@ def workspace_views(plan: Plan, ws):
     return {
         "mu": view(lay["mu"], BH * s.d, torch.float32, 4, (s.B, s.H, s.d)),
         "qnorm": view(lay["qnorm"], BH * N, torch.float32, 4, (s.B, s.H, N)),
-        "rframe": view(lay["rframe"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
+        "rframe": view(lay["rframe"], BH * KF, torch.float32, 4, (s.B, s.H, KF)),
         "rslice": view(lay["rslice"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
         "stat": view(lay["stat"], BH, torch.float32, 4, (s.B, s.H)),
         "elig": view(lay["elig"], BH, torch.uint8, 1, (s.B, s.H)),

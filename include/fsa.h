@@ -31,8 +31,18 @@
  *  - bf16 inputs: the P.V product takes P rounded to bf16, fp32 accumulation
  *    ("Proving the Pixels Didn't Change" ¶2).
  *
+ * Cross-attention. A plan made by fsa_plan_create_cross attends every query
+ * of the chunk to all M tokens of a separate reference set (K and V of
+ * [B][H][M][d]) through the same kernels: the pipeline runs several
+ * attention variants, each with a kernel built for its shape ("The
+ * Workload, and the Port" ¶2). The same route applies: reference keys
+ * centred on their own mean, a fixed per-row shift from the Cauchy-Schwarz
+ * bound over the whole reference set, and the online softmax for loose heads
+ * (or frames, under FSA_MODE_AUTO_FRAME).
+ *
  * Layout. Q, K, V, O are [B][H][N][d] contiguous, d fastest, in the dtype
- * given by the shape; base pointers 16-byte aligned; device memory.
+ * given by the shape; base pointers 16-byte aligned; device memory. For a
+ * cross plan K and V are [B][H][M][d].
  *
  * Ownership. The caller owns Q, K, V, O and the workspace (device memory of
  * fsa_workspace_bytes() bytes, 256-byte aligned). The library never frees
@@ -102,7 +112,9 @@ typedef struct fsa_plan fsa_plan;   /* opaque, host memory only */
 typedef struct {
     size_t mu;      /* key mean, float [B][H][d]                               */
     size_t qnorm;   /* ||q_i||, float [B][H][N]                                */
-    size_t rframe;  /* max_{j in frame g} ||k_j - mu||, float [B][H][F]        */
+    size_t rframe;  /* max_{j in frame g} ||k_j - mu||, float [B][H][F]; for a
+                       cross plan one value per head over the M reference
+                       keys, float [B][H][1]                                   */
     size_t rslice;  /* max over the frames of S(f) of rframe, float [B][H][F]  */
     size_t stat;    /* scale * max_i ||q_i|| rslice(f(i)), float [B][H]        */
     size_t elig;    /* 1 if stat <= FSA_ELIG_BETA else 0, uint8 [B][H]         */
@@ -126,6 +138,22 @@ typedef struct {
  * 2^31 - 1 elements per tensor), FSA_ERR_NOMEM.
  */
 fsa_status fsa_plan_create(const fsa_shape* shape, fsa_plan** out);
+
+/*
+ * fsa_plan_create_cross -- a plan for cross-attention of the chunk's F*T
+ * query tokens to M reference tokens: every query row sees every reference
+ * key ("The Workload, and the Port" ¶2: one kernel per attention variant; the
+ * key set is not frame-structured, so each frame's slice is the whole set and
+ * every tile is live and full). shape->window and shape->ref_frame must be 0;
+ * shape->bk, if not 0, is a multiple of 16 dividing M. fsa_bounds and
+ * fsa_forward then take K and V of [B][H][M][d]; the bounds centre the
+ * reference keys on their own mean and bound every row by
+ * scale * ||q_i|| * max_j ||k_j - mu|| over the whole set ("Unchaining the
+ * Softmax" ¶2-¶3). Errors: as fsa_plan_create, plus FSA_ERR_INVALID_ARG
+ * (M <= 0, window or ref_frame not 0), FSA_ERR_UNSUPPORTED (M % 16 != 0,
+ * B*H*M*d above 2^31 - 1 elements).
+ */
+fsa_status fsa_plan_create_cross(const fsa_shape* shape, int32_t M, fsa_plan** out);
 void fsa_plan_destroy(fsa_plan* plan);
 
 /* The shape a plan was built for, with bq and bk resolved. */
@@ -144,8 +172,13 @@ fsa_status fsa_plan_export(const fsa_plan* plan, int32_t* row_ptr, int32_t* col_
                            int32_t* qframe, int32_t* runs,
                            int32_t* n_qblocks, int64_t* nnz);
 
-/* Valid (query, key) pairs of one (batch, head): T^2 * sum_f |S(f)|. */
+/* Valid (query, key) pairs of one (batch, head): T^2 * sum_f |S(f)|, or
+   N * M for a cross plan. -1 for a NULL plan. */
 int64_t fsa_plan_valid_pairs(const fsa_plan* plan);
+
+/* Key (and value) tokens per (batch, head) the plan's K and V hold: N = F*T,
+   or M for a cross plan. -1 for a NULL plan. */
+int64_t fsa_plan_key_tokens(const fsa_plan* plan);
 
 /* Workspace size in bytes for this plan, and where each product lives. */
 size_t fsa_workspace_bytes(const fsa_plan* plan);
@@ -215,7 +248,23 @@ fsa_status fsa_attention(const void* Q, const void* K, const void* V, void* O,
 size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t window, int32_t ref_frame,
                                      int32_t B, int32_t H, int32_t d, int32_t dtype);
 
-/* Drop every cached plan of fsa_attention. */
+/*
+ * fsa_cross_attention -- fsa_bounds then fsa_forward with a cross plan
+ * (fsa_plan_create_cross, bq = bk = 0) cached per shape: O [B][H][F*T][d] of
+ * the queries Q [B][H][F*T][d] attending to all M reference tokens of
+ * Kr, Vr [B][H][M][d]. Same ownership, workspace and error rules as
+ * fsa_attention; FSA_ERR_INVALID_ARG also for M <= 0.
+ */
+fsa_status fsa_cross_attention(const void* Q, const void* Kr, const void* Vr, void* O,
+                               int32_t F, int32_t T, int32_t M, float scale, int32_t B,
+                               int32_t H, int32_t d, int32_t dtype, int32_t mode, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fsa_cross_attention needs for this shape (0 on invalid input). */
+size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int32_t B, int32_t H,
+                                           int32_t d, int32_t dtype);
+
+/* Drop every cached plan of fsa_attention and fsa_cross_attention. */
 void fsa_cache_clear(void);
 
 const char* fsa_status_string(fsa_status status);

@@ -311,7 +311,7 @@ def attention_two_pass(Q, K, V, F, T, window, ref_frame, scale, b, h, rows,
 
 # --------------------------------------------------------------------------
 # cross-attention to a reference token set: another attention variant of the
-# pipeline ("The Workload, and the Port" ¶3: each attention variant gets a
+# pipeline ("The Workload, and the Port" ¶1-¶2: each attention variant gets a
 # kernel built for its shape; the product conditions on one photo)
 # --------------------------------------------------------------------------
 
@@ -336,6 +336,31 @@ def cross_attention(Q, Kr, Vr, scale: float) -> np.ndarray:
         for h in range(H):
             O[b, h] = cross_attention_rows(Q, Kr, Vr, scale, b, h, np.arange(N))
     return O
+
+
+def cross_plan(F: int, T: int, M: int, bq: int, bk: int) -> dict:
+    """Tile list of cross-attention in the same CSR form as ``plan``: q-blocks
+    of bq chunk tokens against k-blocks of bk reference tokens. Every query
+    row attends to every reference key, so a tile is live iff it holds a
+    valid pair, which every tile does; runs are the one range [0, M)."""
+    if bq % 16 or bk % 16 or T % bq or M % bk:
+        raise ValueError("bq: multiple of 16 dividing T; bk: multiple of 16 dividing M")
+    nqb, nkb = F * T // bq, M // bk
+    mask = np.ones((F * T, M), dtype=bool)        # the definition: every pair attends
+    row_ptr, col_idx, runs = [0], [], []
+    for qb in range(nqb):
+        cols = [kb for kb in range(nkb)
+                if mask[qb * bq:(qb + 1) * bq, kb * bk:(kb + 1) * bk].any()]
+        col_idx.extend(cols)
+        row_ptr.append(len(col_idx))
+        runs.append([(cols[0] * bk, (cols[-1] + 1) * bk)])
+    return {
+        "row_ptr": np.asarray(row_ptr, dtype=np.int64),
+        "col_idx": np.asarray(col_idx, dtype=np.int64),
+        "qframe": np.arange(nqb, dtype=np.int64) * bq // T,
+        "runs": runs,
+        "nnz": len(col_idx),
+    }
 
 
 def cross_bounds(Q, Kr, F: int, T: int, scale: float, beta: float = BETA) -> dict:

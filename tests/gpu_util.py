@@ -35,9 +35,14 @@ class Run:
         if inputs is None:
             inputs = make_inputs(cfg, seed=seed, device="cuda")
         self.Q, self.K, self.V = inputs
-        shape = fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window, cfg.ref_frame,
-                               bq, bk, dtype_code(cfg))
-        self.plan = fsa.fsa_plan_create(shape)
+        if cfg.M:        # cross-attention: K and V hold the M reference tokens
+            shape = fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, 0, 0, bq, bk,
+                                   dtype_code(cfg))
+            self.plan = fsa.fsa_plan_create_cross(shape, cfg.M)
+        else:
+            shape = fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
+                                   cfg.ref_frame, bq, bk, dtype_code(cfg))
+            self.plan = fsa.fsa_plan_create(shape)
         self.ws = torch.zeros(fsa.fsa_workspace_bytes(self.plan), dtype=torch.uint8,
                               device="cuda")
         self.K_before = None
@@ -72,6 +77,14 @@ def oracle_rows(cfg: Config, Q, K, V, b: int, h: int, rows, window=None, ref=Non
     w = cfg.window if window is None else window
     r = cfg.ref_frame if ref is None else ref
     return orc.attention_rows(q, k, v, cfg.F, cfg.T, w, r, cfg.scale, 0, 0, rows)
+
+
+def oracle_cross_rows(cfg: Config, Q, Kr, Vr, b: int, h: int, rows):
+    """Oracle cross-attention rows of head (b, h) for drawn tensors."""
+    q = to_f64(Q[b, h])[None, None]
+    k = to_f64(Kr[b, h])[None, None]
+    v = to_f64(Vr[b, h])[None, None]
+    return orc.cross_attention_rows(q, k, v, cfg.scale, 0, 0, rows)
 
 
 def errors(got: torch.Tensor, want: np.ndarray):

@@ -125,3 +125,61 @@ def test_attention_validates_before_launch():
             call(**over)
         assert e.value.status == status, (over, fsa.fsa_last_error())
     fsa.fsa_cache_clear()
+
+
+@pytest.mark.parametrize("kw,M,status", [
+    (dict(), 0, fsa.FSA_ERR_INVALID_ARG),
+    (dict(), -16, fsa.FSA_ERR_INVALID_ARG),
+    (dict(), 40, fsa.FSA_ERR_UNSUPPORTED),           # M % 16 != 0
+    (dict(window=1), 64, fsa.FSA_ERR_INVALID_ARG),    # no window in cross-attention
+    (dict(ref_frame=1), 64, fsa.FSA_ERR_INVALID_ARG),
+    (dict(bk=32), 48, fsa.FSA_ERR_INVALID_ARG),       # 32 does not divide M = 48
+    (dict(bk=32), 96, None),                          # 32 divides M = 96, though not T = 48
+    (dict(T=40), 64, fsa.FSA_ERR_UNSUPPORTED),
+    (dict(H=2000, d=128), 1 << 20, fsa.FSA_ERR_UNSUPPORTED),   # > 2^31 key elements
+])
+def test_cross_plan_create_errors(kw, M, status):
+    base = dict(window=0)
+    base.update(kw)
+    if status is None:
+        p = fsa.fsa_plan_create_cross(shape(**base), M)
+        assert fsa.fsa_plan_shape(p).bk == kw["bk"]
+        return
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.fsa_plan_create_cross(shape(**base), M)
+    assert e.value.status == status
+    assert fsa.fsa_last_error()
+
+
+def test_cross_attention_validates_before_launch():
+    F, T, M, B, H, d = 5, 48, 720, 1, 2, 64
+    need = fsa.fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, fsa.FSA_F32)
+    assert B * H * F * T * 4 < need < B * H * F * T * d * 4
+    names = ["Q", "Kr", "Vr", "O", "F", "T", "M", "scale", "B", "H", "d", "dtype", "mode",
+             "ws", "ws_bytes"]
+    base = [FAKE, FAKE * 64, FAKE * 128, FAKE * 256, F, T, M, 0.125, B, H, d, fsa.FSA_F32, 0,
+            FAKE * 512, need]
+
+    def call(**over):
+        args = list(base)
+        for k, v in over.items():
+            args[names.index(k)] = v
+        fsa.fsa_cross_attention(*args, stream=0)
+    kv = B * H * M * d * 4
+    for over, status in [
+        (dict(ws_bytes=need - 1), fsa.FSA_ERR_WORKSPACE),
+        (dict(ws=None), fsa.FSA_ERR_WORKSPACE),
+        (dict(M=0), fsa.FSA_ERR_INVALID_ARG),
+        (dict(M=24), fsa.FSA_ERR_UNSUPPORTED),
+        (dict(T=40), fsa.FSA_ERR_UNSUPPORTED),
+        (dict(scale=0.0), fsa.FSA_ERR_INVALID_ARG),
+        (dict(mode=7), fsa.FSA_ERR_INVALID_ARG),
+        (dict(Vr=None), fsa.FSA_ERR_INVALID_ARG),
+        (dict(O=FAKE * 64 + kv - 256), fsa.FSA_ERR_INVALID_ARG),   # O overlaps the end of Kr
+    ]:
+        with pytest.raises(fsa.FsaError) as e:
+            call(**over)
+        assert e.value.status == status, (over, fsa.fsa_last_error())
+    with pytest.raises(fsa.FsaError):
+        fsa.fsa_cross_attention_workspace_bytes(F, T, 0, B, H, d, fsa.FSA_F32)
+    fsa.fsa_cache_clear()

@@ -1,0 +1,162 @@
+"""Cross-attention through the same kernels vs the fp64 oracle (GPU).
+
+Every query row of the chunk attends to all M reference tokens. Bar as for
+self-attention: flags bit-exact; bf16 outputs within max-abs 2e-2 and
+mean-abs 2e-3; fp32 within max-abs 1e-5. The small workload has a loose head
+(one reference key scaled x20) that must take the online route.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fsa_oracle as orc
+from frame_aligned_block_amd import fsa
+from frame_aligned_block_amd.inputs import CONFIGS, to_f64
+
+from gpu_util import BF16_MAX_ABS, Run, assert_close, errors, oracle_cross_rows, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU too; every test here is gpu-marked
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def check_cross_bounds(run: Run, heads):
+    cfg = run.cfg
+    v = run.views()
+    for h in heads:
+        q = to_f64(run.Q[0, h])[None, None]
+        k = to_f64(run.K[0, h])[None, None]
+        want = orc.cross_bounds(q, k, cfg.F, cfg.T, cfg.scale)
+        mu = v["mu"][0, h].double().cpu().numpy()
+        assert np.max(np.abs(mu - want["mu"][0, 0])) < 1e-4, h
+        qn = v["qnorm"][0, h].double().cpu().numpy()
+        assert np.allclose(qn, want["qnorm"][0, 0], rtol=2e-6, atol=1e-6), h
+        rtol = 1e-5
+        R = float(want["R"][0, 0])
+        assert v["rframe"].shape == (1, cfg.H, 1)
+        assert float(v["rframe"][0, h, 0]) == pytest.approx(R, rel=rtol), h
+        assert np.allclose(v["rslice"][0, h].double().cpu().numpy(), R, rtol=rtol), h
+        assert float(v["stat"][0, h]) == pytest.approx(want["stat"][0, 0], rel=rtol), h
+        sf = v["statf"][0, h].double().cpu().numpy()
+        assert np.allclose(sf, want["stat_frame"][0, 0], rtol=rtol), h
+        # flags bit-exact, every statistic clear of the threshold by 5%
+        assert abs(want["stat"][0, 0] - orc.BETA) / orc.BETA > 0.05, h
+        assert np.all(np.abs(want["stat_frame"][0, 0] - orc.BETA) / orc.BETA > 0.05), h
+        assert int(v["elig"][0, h]) == int(want["elig"][0, 0]), h
+        assert np.array_equal(v["eligf"][0, h].cpu().numpy().astype(bool),
+                              want["elig_frame"][0, 0]), h
+
+
+def test_cross_bounds_parity_small():
+    cfg = CONFIGS["xref-small"]
+    say("cross bounds", cfg.name)
+    run = Run(cfg).bounds()
+    torch.cuda.synchronize()
+    check_cross_bounds(run, range(cfg.H))
+    elig = run.views()["elig"][0].cpu().numpy()
+    assert list(elig) == [0 if cfg.is_loose(h) else 1 for h in range(cfg.H)]
+    host = fsa.fsa_copy_eligibility(run.plan, run.ws)
+    assert np.array_equal(host[0], elig)
+
+
+def test_cross_small_full():
+    """Every mode on the whole small workload; the loose head takes the online
+    route bit-identically under AUTO and ONLINE_ONLY."""
+    cfg = CONFIGS["xref-small"]
+    say("cross forward", cfg.name)
+    run = Run(cfg).bounds()
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.cross_attention(Q, K, V, cfg.scale)
+    outs = {}
+    for mode in ("auto", "online", "auto_frame"):
+        outs[mode] = run.forward(mode)
+        mx, mean = assert_close(cfg, outs[mode], want, f"cross small {mode}")
+        print(f"cross small {mode}: max {mx:.3g} mean {mean:.3g}")
+    for h in range(cfg.H):
+        if cfg.is_loose(h):
+            assert torch.equal(outs["auto"][0, h], outs["online"][0, h]), h
+        else:
+            d = (outs["auto"][0, h].float() - outs["online"][0, h].float()).abs()
+            assert float(d.max()) <= BF16_MAX_ABS, h
+    # the loose head's fixed route underflows: why the fallback exists
+    O = run.forward("fixed")
+    h = next(h for h in range(cfg.H) if cfg.is_loose(h))
+    mx, _, finite = errors(O[0, h], want[0, h])
+    assert (not finite) or mx > BF16_MAX_ABS
+
+
+def test_cross_720p_sampled():
+    """The benchmarked cross workload, in the launch configuration it is timed in."""
+    cfg = CONFIGS["720p-xref"]
+    say("cross forward", cfg.name)
+    run = Run(cfg).bounds()
+    O = run.forward("auto")
+    assert bool(torch.isfinite(O).all())
+    assert int(run.views()["elig"].min()) == 1
+    rng = np.random.default_rng(5)
+    for h in (0, 11, 23):
+        edges = np.concatenate([[f * cfg.T, f * cfg.T + cfg.T - 1] for f in range(cfg.F)])
+        rows = np.unique(np.concatenate([edges, rng.choice(cfg.N, 150, replace=False)]))
+        want = oracle_cross_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+        mx, mean = assert_close(cfg, O[0, h, rows], want, f"720p-xref head {h}")
+        print(f"720p-xref h{h}: max {mx:.3g} mean {mean:.3g}")
+
+
+@pytest.mark.parametrize("M", [16, 48, 720, 3600])
+def test_cross_probe_granule_counts(M):
+    """Q = 0 and V_j = one-hot((j // 16) mod d): every row's output is the
+    share of each granule class among the M reference keys, known exactly,
+    so a dropped or doubled 16-key granule shows up far above bf16 rounding
+    (M = 720 and 3600 end in a lone granule after whole 64-key chunks)."""
+    cfg = CONFIGS["xref-small"].with_(H=1, M=M, loose_period=0)
+    say("cross probe", M)
+    shape = (1, 1, cfg.N, cfg.d)
+    g = torch.Generator(device="cuda").manual_seed(M)
+    Q = torch.zeros(shape, device="cuda", dtype=torch.bfloat16)
+    K = (torch.randn((1, 1, M, cfg.d), generator=g, device="cuda") + 2.0).to(torch.bfloat16)
+    V = torch.zeros((1, 1, M, cfg.d), device="cuda", dtype=torch.bfloat16)
+    idx = torch.arange(M, device="cuda")
+    V[0, 0, idx, (idx // 16) % cfg.d] = 1
+    run = Run(cfg, inputs=(Q, K, V)).bounds()
+    O = run.forward()[0, 0].double().cpu().numpy()
+    want = np.bincount((np.arange(M) // 16) % cfg.d, minlength=cfg.d) / M
+    assert np.max(np.abs(O - want[None, :])) <= 4e-3 * want.max()
+
+
+CROSS_EDGE = [
+    # name, F, T, M, H, d, dtype
+    ("one-granule-set", 3, 64, 16, 2, 128, "bf16"),
+    ("short-set", 4, 48, 48, 2, 128, "bf16"),
+    ("ragged-set", 3, 880, 1040, 2, 128, "bf16"),     # 16 chunks of 64, then 16 keys
+    ("d64-bf16", 5, 240, 112, 3, 64, "bf16"),
+    ("f32-d64", 5, 48, 80, 2, 64, "f32"),
+    ("f32-d128", 4, 32, 64, 2, 128, "f32"),
+    ("batch-2", 4, 144, 160, 3, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CROSS_EDGE, ids=[c[0] for c in CROSS_EDGE])
+def test_cross_edge_shapes(case):
+    name, F, T, M, H, d, dt = case
+    cfg = CONFIGS["xref-small"].with_(name=name, F=F, T=T, M=M, H=H, d=d, dtype=dt,
+                                      loose_period=0, B=2 if name == "batch-2" else 1)
+    say("cross edge", case)
+    run = Run(cfg).bounds()
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.cross_attention(Q, K, V, cfg.scale)
+    for mode in ("auto", "online"):
+        assert_close(cfg, run.forward(mode), want, f"{name} {mode}")
+
+
+def test_cross_attention_entry_point():
+    cfg = CONFIGS["xref-small"]
+    say("fsa_cross_attention")
+    run = Run(cfg)
+    O = fsa.cross_attention(run.Q, run.K, run.V, cfg.F, cfg.T)
+    torch.cuda.synchronize()
+    run.bounds()
+    assert torch.equal(run.forward(), O)
+    rows = np.arange(0, cfg.N, 7)
+    want = oracle_cross_rows(cfg, run.Q, run.K, run.V, 0, 1, rows)
+    assert_close(cfg, O[0, 1, rows], want, "fsa_cross_attention")

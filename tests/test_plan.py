@@ -62,3 +62,57 @@ def test_workspace_layout_is_aligned_and_disjoint():
         assert e0 <= a1
     assert all(lay[k] % 256 == 0 for k in sizes)
     assert lay["total"] == fsa.fsa_workspace_bytes(p) >= spans[-1][1]
+
+
+# ------------------------------------------------------------------ cross-attention plans
+
+CROSS = [
+    # F, T, M, bq, bk
+    (5, 48, 720, 16, 16), (5, 48, 720, 48, 80), (13, 3600, 3600, 48, 144),
+    (4, 880, 720, 80, 48), (1, 16, 16, 16, 16), (9, 8160, 48, 96, 48),
+]
+
+
+def cross_plan(F, T, M, bq, bk, d=128, dtype=fsa.FSA_BF16, B=1, H=1):
+    return fsa.fsa_plan_create_cross(fsa.make_shape(B, H, F, T, d, 0, 0, bq, bk, dtype), M)
+
+
+@pytest.mark.parametrize("F,T,M,bq,bk", CROSS)
+def test_cross_plan_bit_exact_vs_oracle(F, T, M, bq, bk):
+    p = cross_plan(F, T, M, bq, bk)
+    got = fsa.fsa_plan_export(p)
+    want = orc.cross_plan(F, T, M, bq, bk)
+    # closed form: every tile of the (F*T/bq) x (M/bk) grid is live
+    assert got["nnz"] == want["nnz"] == (F * T // bq) * (M // bk)
+    assert np.array_equal(got["row_ptr"], want["row_ptr"])
+    assert np.array_equal(got["col_idx"], want["col_idx"])
+    assert np.array_equal(got["qframe"], want["qframe"])
+    assert np.all(got["runs"] == np.array([0, M, 0, 0]))
+    assert fsa.fsa_plan_valid_pairs(p) == F * T * M
+    assert fsa.fsa_plan_key_tokens(p) == M
+
+
+def test_key_tokens_of_self_plan():
+    assert fsa.fsa_plan_key_tokens(plan(13, 3600, 2, 0, 0, 0)) == 13 * 3600
+
+
+def test_cross_auto_block_sizes():
+    s = fsa.fsa_plan_shape(cross_plan(13, 3600, 720, 0, 0))
+    assert s.bq == 48 and s.bk == 48          # 720 = 16 * 45: 48 is the largest <= 64
+    s = fsa.fsa_plan_shape(cross_plan(4, 880, 16, 0, 0))
+    assert s.bk == 16
+
+
+def test_cross_workspace_layout():
+    H, F, T, M = 24, 13, 3600, 3600
+    p = cross_plan(F, T, M, 0, 0, H=H)
+    lay = fsa.fsa_workspace_layout(p)
+    # one key radius per head (H floats, padded to 256 bytes); per-frame slice
+    # radii as for self-attention
+    assert lay["rslice"] - lay["rframe"] == 256
+    sizes = {"mu": H * 128 * 4, "qnorm": H * F * T * 4, "rframe": H * 4, "rslice": H * F * 4,
+             "stat": H * 4, "elig": H, "statf": H * F * 4, "eligf": H * F}
+    spans = sorted((lay[k], lay[k] + n) for k, n in sizes.items())
+    for (a0, e0), (a1, _) in zip(spans, spans[1:]):
+        assert e0 <= a1
+    assert lay["total"] == fsa.fsa_workspace_bytes(p) >= spans[-1][1]
