@@ -592,6 +592,120 @@ __device__ __forceinline__ void copy_only(unsigned char* smem, const Slice& sl, 
     FSA_WAIT_VMCNT(0);
 }
 
+// The slice walk of a workgroup whose frame has a single row unit left for it
+// (T = 3600 leaves one 16-row granule after 28 full workgroups): rather than
+// one wave computing while the others only stage keys, every wave takes the
+// same unit, and wave w computes on the w-th 16-key granule of every chunk,
+// all waves staging and passing the barriers as usual. Each wave ends with
+// partial sums over its granules (and, on the online route, its running
+// max), which combine_split adds up.
+template <int D, int G, bool FIXED>
+__device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& sl,
+                                             const __bf16* Kh, const __bf16* Vh,
+                                             const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
+                                             float c, f32x4 (&o)[G][D / 16], float (&rs)[G],
+                                             float (&m)[G], int wave, int lane) {
+    using GG = Geo<D>;
+    const LaneAddr la = lane_addr(lane & 15, lane >> 4);
+    const int nchunks = (sl.total + kBK - 1) / kBK;
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+    const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
+    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    FSA_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
+    int st = 0;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        if (ch * kBK + 16 * wave < sl.total) {                  // this wave's granule exists
+            const unsigned char* S0 = smem + st * GG::STAGE;
+            f32x4 sv[2][G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            scores<D, G, 1>(S0, 16 * wave, qf, sv, la);
+            bf16x2 pk[G][2];
+            softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+            pv_half<D, G>(S0 + GG::TILE, 16 * wave, pk, o, la);
+        }
+        if (ch + 1 < nchunks) {
+            FSA_WAIT_VMCNT(0);                                  // chunk ch+1 has landed
+            FSA_WAIT_LGKM0();                                   // no read of the old stage is pending
+            __builtin_amdgcn_s_barrier();
+            if (ch + 2 < nchunks)
+                issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+            st ^= 1;
+        }
+    }
+    FSA_WAIT_VMCNT(0);
+}
+
+// Floats per lane that a wave of a split workgroup hands over: its partial
+// output accumulators, row sums and running maxima.
+template <int D, int G>
+constexpr int split_floats() { return G * (D / 16) * 4 + 2 * G; }
+
+// Adds the partial results of a split workgroup's waves into wave 0, in
+// wave order (so the sum is deterministic), through the LDS the key ring used.
+// The fixed route's partial sums share one shift and simply add; the online
+// route rescales each to the largest running max first. Returns true in wave
+// 0 only, which then holds the whole row sums and accumulators.
+template <int D, int G>
+__device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G][D / 16],
+                                              float (&rs)[G], float (&m)[G], float c, bool fixed,
+                                              int wave, int lane) {
+    constexpr int NF = split_floats<D, G>();
+    float* buf = reinterpret_cast<float*>(smem);
+    FSA_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();                               // the key ring is no longer read
+    if (wave > 0) {
+        float* mine = buf + (wave - 1) * NF * 64 + lane;
+        int i = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mine[64 * i++] = o[g][db][e];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mine[64 * i++] = rs[g];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mine[64 * i++] = m[g];
+    }
+    __builtin_amdgcn_s_barrier();
+    if (wave > 0) return false;
+    for (int w = 1; w < fsa::kWaves; ++w) {
+        const float* theirs = buf + (w - 1) * NF * 64 + lane;
+        constexpr int RS = G * (D / 16) * 4, MX = RS + G;
+        if (fixed) {
+            int i = 0;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[g][db][e] += theirs[64 * i++];
+#pragma unroll
+            for (int g = 0; g < G; ++g) rs[g] += theirs[64 * (RS + g)];
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float mw = theirs[64 * (MX + g)];
+                const float mx = fmaxf(m[g], mw);               // wave 0's max is finite
+                const float a = __builtin_amdgcn_exp2f((m[g] - mx) * c);
+                const float b = __builtin_amdgcn_exp2f((mw - mx) * c);   // 0 for a wave with no chunk
+                m[g] = mx;
+                rs[g] = rs[g] * a + theirs[64 * (RS + g)] * b;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[g][db][e] = o[g][db][e] * a + theirs[64 * ((g * (D / 16) + db) * 4 + e)] * b;
+            }
+        }
+    }
+    return true;
+}
+
 // Workgroups per CU for two waves per SIMD (<= 256 registers per lane) while
 // a wave's accumulators and query fragments fit, else one wave per SIMD.
 constexpr int fwd_occupancy(int D, int G) {
@@ -601,7 +715,10 @@ constexpr int fwd_occupancy(int D, int G) {
 template <int D, int G>
 __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {
     using GG = Geo<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * GG::STAGE];
+    // the key ring; a split workgroup reuses it to combine its waves' partials
+    constexpr int kSplitBytes = (fsa::kWaves - 1) * split_floats<D, G>() * 64 * 4;
+    __shared__ __attribute__((aligned(16)))
+        unsigned char smem[2 * GG::STAGE > kSplitBytes ? 2 * GG::STAGE : kSplitBytes];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
@@ -625,8 +742,12 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     // frame (the tail of a frame whose granule count G does not divide)
     // repeat the frame's last granule and are not stored: every computing
     // wave runs the same loop, with no predicate inside it. A wave wholly
-    // past the last unit only helps stage the keys.
-    const int unit = gq * fsa::kWaves + wave;
+    // past the last unit only helps stage the keys, except in a workgroup
+    // left with a single unit: there every wave takes that unit and a share
+    // of the key chunks (attend_split).
+    const int first_unit = gq * fsa::kWaves;
+    const bool split = kBK == 16 * fsa::kWaves && p.units_per_frame - first_unit == 1;   // uniform
+    const int unit = split ? first_unit : first_unit + wave;
     const int ngran = T >> 4;
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
@@ -673,10 +794,18 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 #pragma unroll
     for (int g = 0; g < G; ++g) shift[g] *= c;
 
-    if (fixed)
+    if (split) {
+        float m[G];
+        if (fixed)
+            attend_split<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        else
+            attend_split<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        if (!combine_split<D, G>(smem, o, rs, m, c, fixed, uwave, lane)) return;
+    } else if (fixed) {
         attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
-    else
+    } else {
         attend<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+    }
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
