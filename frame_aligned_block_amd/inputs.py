@@ -50,6 +50,7 @@ class Config:
     loose_frames: tuple = ()  # frames holding a loose head's outlier key; () = every frame
     B: int = 1
     M: int = 0        # cross-attention: reference tokens every query attends to (0 = self)
+    grid: tuple = ()  # (Hg, Wg) latent patch grid of a frame (T = Hg*Wg); producer workloads
 
     @property
     def N(self) -> int:
@@ -106,6 +107,14 @@ CONFIGS = {
     "xref-small": Config("xref-small", F=4, T=880, H=4, d=128, dtype="bf16", window=0,
                          ref_frame=0, shared_mean=True, M=720, loose_period=4,
                          loose_phase=3),
+    # Producer workloads: the tokens of a chunk (C = H*d channels) go through
+    # RMSNorm, the Q/K/V projection, 3-D rotary embedding and head packing
+    # into the attention's layout. The 720p one is the SR transformer layer
+    # that feeds the 720p attention (45x80 patches per frame, 24 heads of 128).
+    "prep-small": Config("prep-small", F=4, T=880, H=4, d=128, dtype="bf16", window=2,
+                         ref_frame=0, shared_mean=True, grid=(22, 40)),
+    "720p-prep": Config("720p-prep", F=13, T=3600, H=24, d=128, dtype="bf16", window=2,
+                        ref_frame=0, shared_mean=True, grid=(45, 80)),
 }
 
 
@@ -171,6 +180,31 @@ def make_inputs(cfg: Config, seed: int = 0, device="cpu"):
             q, k, v = draw(cfg, seed, b, h, device)
             Q[b, h], K[b, h], V[b, h] = q, k, v
     return Q, K, V
+
+
+def make_prep_inputs(cfg: Config, seed: int = 0, device="cpu"):
+    """Draw the producer's inputs for a workload with a grid: tokens X
+    [B, N, C] (bf16), the joint projection W [3C, C] (bf16, (out, in)
+    convention) and the RMSNorm weight gamma [C] (float32), C = H*d.
+
+    Draw order from one generator seeded with head_seed(seed, 4095, 4095):
+    gamma = 1 + 0.1 N(0,1); W = N(0,1) / sqrt(C); then per batch b:
+    z = N(0,1) [N, C] and a shared offset c = N(0,1) [1, C] (shared-mean
+    workloads), x = z + c. The shared offset gives the keys the common
+    component that centring removes."""
+    C = cfg.H * cfg.d
+    g = torch.Generator(device=device)
+    g.manual_seed(head_seed(seed, 4095, 4095))
+    kw = dict(generator=g, device=device, dtype=torch.float32)
+    gamma = 1.0 + 0.1 * torch.randn((C,), **kw)
+    W = (torch.randn((3 * C, C), **kw) / math.sqrt(C)).to(torch.bfloat16)
+    X = torch.empty((cfg.B, cfg.N, C), dtype=torch.bfloat16, device=device)
+    for b in range(cfg.B):
+        x = torch.randn((cfg.N, C), **kw)
+        if cfg.shared_mean:
+            x += torch.randn((1, C), **kw)
+        X[b] = x.to(torch.bfloat16)
+    return X, W, gamma
 
 
 def to_f64(t: torch.Tensor):
