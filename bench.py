@@ -145,6 +145,104 @@ def calibrate_copy(nbytes: int) -> None:
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 5}))
 
 
+def timed(fn, launches: int, stream):
+    """Median HIP-event time (ms) of `launches` calls of fn on `stream`."""
+    import torch
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    e[0].record(stream)
+    for i in range(launches):
+        fn()
+        e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.median([e[i].elapsed_time(e[i + 1]) for i in range(launches)])
+
+
+def bench_producer(args, cfg) -> int:
+    """A producer workload: one step is fsa_prep (RMSNorm, Q/K/V projection,
+    rotary embedding, head packing, and the bounds' row norms and key sums),
+    fsa_bounds_after_prep, then fsa_forward, from tokens already in HBM. The
+    roofline line is the producer kernel's (MFMA-bound projection); the same
+    chain with the separate fsa_bounds pass is timed beside it."""
+    import torch
+    from frame_aligned_block_amd import fsa
+    from frame_aligned_block_amd.inputs import make_prep_inputs
+
+    print(f"[bench] {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
+    X, W, g = make_prep_inputs(cfg, seed=0, device="cuda")
+    Wp = torch.empty_like(W)
+    fsa.fsa_prep_pack_weights(W, g, Wp, cfg.H, cfg.d)
+    plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
+                                              cfg.ref_frame, args.bq, 0, fsa.FSA_BF16))
+    ws = torch.zeros(fsa.fsa_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    shape = (cfg.B, cfg.H, cfg.N, cfg.d)
+    Q, K, V, O = (torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    Hg, Wg = cfg.grid
+    stream = torch.cuda.current_stream()
+    C = cfg.H * cfg.d
+    proj_flops = 2.0 * cfg.B * cfg.N * C * 3 * C
+    attn_flops = 4.0 * cfg.d * fsa.fsa_plan_valid_pairs(plan) * cfg.B * cfg.H
+
+    def prep():
+        fsa.fsa_prep(plan, Hg, Wg, X, Wp, Q, K, V, ws, stream)
+
+    def step():
+        prep()
+        fsa.fsa_bounds_after_prep(plan, K, ws, cfg.scale, stream)
+        fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, args.mode, stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    n = max(3, args.steps // 2)
+    prep_ms = timed(prep, n, stream)
+    bap_ms = timed(lambda: fsa.fsa_bounds_after_prep(plan, K, ws, cfg.scale, stream), n, stream)
+    bounds_ms = timed(lambda: fsa.fsa_bounds(plan, Q, K, ws, cfg.scale, stream), n, stream)
+    fsa.fsa_bounds_after_prep(plan, K, ws, cfg.scale, stream)
+    fwd_ms = timed(lambda: fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, args.mode, stream),
+                   n, stream)
+    elig = float(fsa.fsa_copy_eligibility(plan, ws, stream).mean())
+    achieved = proj_flops / prep_ms / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round((proj_flops + attn_flops) / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: the SR layer's producer then attention: "
+                               f"F={cfg.F} frames of {Hg}x{Wg} patches ({cfg.N} tokens), "
+                               f"C={C} channels, H={cfg.H}, d={cfg.d}, bf16, window "
+                               f"+-{cfg.window} + reference frame {cfg.ref_frame}",
+                   "B": cfg.B, "H": cfg.H, "F": cfg.F, "T": cfg.T, "d": cfg.d, "C": C,
+                   "grid": [Hg, Wg], "mode": args.mode,
+                   "projection_flops": proj_flops, "attention_valid_flops": attn_flops},
+        "prep_ms_median": round(prep_ms, 4),
+        "bounds_after_prep_ms_median": round(bap_ms, 4),
+        "separate_bounds_ms_median": round(bounds_ms, 4),
+        "forward_ms_median": round(fwd_ms, 4),
+        "eligible_head_fraction": round(elig, 4),
+        "roofline": {"kernel": "prep_qkv", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +276,8 @@ def main() -> int:
     from frame_aligned_block_amd.inputs import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    if cfg.grid:
+        return bench_producer(args, cfg)
     print(f"[bench] {cfg.name}: drawing inputs", file=sys.stderr, flush=True)
     Q, K, V = make_inputs(cfg, seed=0, device="cuda")
     code = fsa.FSA_BF16 if cfg.dtype == "bf16" else fsa.FSA_F32

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfsa.so")
-SOURCES = ["plan.cpp", "abi.cpp", "bounds.hip", "forward.hip"]
+SOURCES = ["plan.cpp", "abi.cpp", "bounds.hip", "forward.hip", "prep.hip"]
 ARCH = "gfx950"
 
 

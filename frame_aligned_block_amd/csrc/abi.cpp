@@ -286,3 +286,112 @@ extern "C" fsa_status fsa_cross_attention(const void* Q, const void* Kr, const v
     return attend("fsa_cross_attention", Q, Kr, Vr, O, make_shape(F, T, 0, 0, B, H, d, dtype), M,
                   scale, mode, ws, ws_bytes, stream);
 }
+
+// ------------------------------------------------------------------ producer
+
+namespace {
+
+bool prep_shape_ok(const fsa_plan& p, const char* who) {
+    const fsa_shape& s = p.shape;
+    if (p.cross) {
+        set_error("%s: the producer makes self-attention inputs; the plan is a cross plan", who);
+        return false;
+    }
+    if (s.d != 128 || s.dtype != FSA_BF16) {
+        set_error("%s: the producer supports d = 128, bf16 (got d=%d dtype=%d)", who, s.d,
+                  s.dtype);
+        return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" size_t fsa_prep_weight_bytes(int32_t H, int32_t d) {
+    if (H < 1 || d < 1) return 0;
+    const size_t C = size_t(H) * d;
+    return 3 * C * C * 2;
+}
+
+extern "C" fsa_status fsa_prep_pack_weights(const void* W, const float* gamma, void* Wp, int32_t H,
+                                            int32_t d, hipStream_t stream) {
+    if (!W || !gamma || !Wp) {
+        set_error("fsa_prep_pack_weights: NULL W, gamma or Wp");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (H < 1 || d != 128) {
+        set_error("fsa_prep_pack_weights: H=%d must be >= 1 and d=%d must be 128", H, d);
+        return d != 128 && H >= 1 ? FSA_ERR_UNSUPPORTED : FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(W, 16) || !aligned(Wp, 16) || !aligned(gamma, 4)) {
+        set_error("fsa_prep_pack_weights: W and Wp must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    const size_t nb = fsa_prep_weight_bytes(H, d);
+    if (overlaps(W, nb, Wp, nb)) {
+        set_error("fsa_prep_pack_weights: Wp overlaps W");
+        return FSA_ERR_INVALID_ARG;
+    }
+    return fsa::launch_prep_fold(W, gamma, Wp, H * d, stream);
+}
+
+extern "C" fsa_status fsa_prep(const fsa_plan* plan, int32_t grid_h, int32_t grid_w,
+                               const void* X, const void* Wp, void* Q, void* K, void* V,
+                               void* ws, hipStream_t stream) {
+    if (!plan || !X || !Wp || !Q || !K || !V) {
+        set_error("fsa_prep: NULL plan, X, Wp, Q, K or V");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!prep_shape_ok(*plan, "fsa_prep")) return FSA_ERR_UNSUPPORTED;
+    const fsa_shape& s = plan->shape;
+    if (grid_h < 1 || grid_w < 1 || int64_t(grid_h) * grid_w != s.T) {
+        set_error("fsa_prep: grid %d x %d does not hold T=%d tokens", grid_h, grid_w, s.T);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(X, 16) || !aligned(Wp, 16) || !aligned(Q, 16) || !aligned(K, 16) ||
+        !aligned(V, 16)) {
+        set_error("fsa_prep: X, Wp, Q, K and V must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!ws || !aligned(ws, 256)) {
+        set_error("fsa_prep: workspace missing or not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    const size_t nb = tensor_bytes(*plan), wb = fsa_prep_weight_bytes(s.H, s.d);
+    const void* outs[3] = {Q, K, V};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], nb, X, nb) || overlaps(outs[i], nb, Wp, wb) ||
+            overlaps(outs[i], nb, ws, plan->ws.total)) {
+            set_error("fsa_prep: an output overlaps X, Wp or the workspace");
+            return FSA_ERR_INVALID_ARG;
+        }
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], nb, outs[j], nb)) {
+                set_error("fsa_prep: Q, K and V overlap");
+                return FSA_ERR_INVALID_ARG;
+            }
+    }
+    return fsa::launch_prep(*plan, grid_w, X, Wp, Q, K, V, ws, stream);
+}
+
+extern "C" fsa_status fsa_bounds_after_prep(const fsa_plan* plan, const void* K, void* ws,
+                                            float scale, hipStream_t stream) {
+    if (!plan || !K) {
+        set_error("fsa_bounds_after_prep: NULL plan or K");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!prep_shape_ok(*plan, "fsa_bounds_after_prep")) return FSA_ERR_UNSUPPORTED;
+    if (!good_scale(scale)) {
+        set_error("fsa_bounds_after_prep: scale must be finite and > 0 (got %g)", double(scale));
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!aligned(K, 16)) {
+        set_error("fsa_bounds_after_prep: K must be 16-byte aligned");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (!ws || !aligned(ws, 256)) {
+        set_error("fsa_bounds_after_prep: workspace missing or not 256-byte aligned");
+        return FSA_ERR_WORKSPACE;
+    }
+    return fsa::launch_bounds_after_prep(*plan, K, ws, scale, stream);
+}

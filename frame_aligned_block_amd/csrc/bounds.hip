@@ -264,7 +264,24 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
     hipLaunchKernelGGL((bounds_mean<D>), dim3(BH), dim3(256), 0, stream, colsum, mu, NK, kp.count);
     hipLaunchKernelGGL((bounds_radius<E, D>), dim3(kp.count, BH), dim3(256), 0, stream, K, mu,
                        partmax, NK, kp);
-    hipLaunchKernelGGL(bounds_finalize, dim3(BH), dim3(256), 0, stream, partqmax, partmax,
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return fsa::launch_bounds_finalize(p, ws, scale, stream);
+}
+
+}  // namespace
+
+namespace fsa {
+
+fsa_status launch_bounds_finalize(const fsa_plan& p, char* ws, float scale, hipStream_t stream) {
+    const fsa_shape& s = p.shape;
+    const PartsArg qp = parts_arg(p.bounds.q), kp = parts_arg(p.bounds.k);
+    hipLaunchKernelGGL(bounds_finalize, dim3(s.B * s.H), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(ws + p.bounds.partqmax),
+                       reinterpret_cast<const float*>(ws + p.bounds.partmax),
                        reinterpret_cast<float*>(ws + p.ws.rframe),
                        reinterpret_cast<float*>(ws + p.ws.rslice),
                        reinterpret_cast<float*>(ws + p.ws.stat),
@@ -274,15 +291,11 @@ fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* w
                        scale, p.table);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
-        fsa::set_error("fsa_bounds: launch failed: %s", hipGetErrorString(err));
+        set_error("bounds: launch failed: %s", hipGetErrorString(err));
         return FSA_ERR_HIP;
     }
     return FSA_OK;
 }
-
-}  // namespace
-
-namespace fsa {
 
 fsa_status launch_bounds(const fsa_plan& p, const void* Q, const void* K, void* ws, float scale,
                          hipStream_t stream) {

@@ -76,9 +76,16 @@ struct fsa_plan {
     fsa::BoundsGeometry bounds;
     fsa::ForwardGeometry forward;
     fsa_ws_layout ws;
+    size_t prep_ksum = 0;            // private ws: producer's key column sums, [BH][tiles][d]
 };
 
 namespace fsa {
+
+// The producer's RMSNorm epsilon and rotary base.
+constexpr float kPrepEps = 1e-6f;
+constexpr double kPrepBase = 10000.0;
+// Tokens per producer tile (the key column sums are kept per tile).
+constexpr int kPrepTile = 128;
 
 // Thread-local last-error text (abi.cpp).
 void set_error(const char* fmt, ...);
@@ -88,6 +95,15 @@ fsa_status launch_bounds(const fsa_plan& plan, const void* Q, const void* K, voi
                          float scale, hipStream_t stream);
 fsa_status launch_forward(const fsa_plan& plan, const void* Q, const void* K, const void* V,
                           void* O, const void* ws, float scale, int32_t mode, hipStream_t stream);
+// Per-frame and per-slice radii, statistics and flags from the per-part maxima.
+fsa_status launch_bounds_finalize(const fsa_plan& plan, char* ws, float scale, hipStream_t stream);
+// The producer (prep.hip).
+fsa_status launch_prep_fold(const void* W, const float* gamma, void* Wp, int32_t C,
+                            hipStream_t stream);
+fsa_status launch_prep(const fsa_plan& plan, int32_t grid_w, const void* X, const void* Wp,
+                       void* Q, void* K, void* V, void* ws, hipStream_t stream);
+fsa_status launch_bounds_after_prep(const fsa_plan& plan, const void* K, void* ws, float scale,
+                                    hipStream_t stream);
 
 inline int32_t frame_order_at(const FrameTable& t, int32_t i) {
     return (t.order[i >> 2] >> (8 * (i & 3))) & 0xff;

@@ -224,6 +224,10 @@ fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const c
         p->bounds.colsum = off;  off = align_up(off + BH * nkparts * s.d * 4);
         p->bounds.partmax = off; off = align_up(off + BH * nkparts * 4);
         p->bounds.partqmax = off; off = align_up(off + BH * nqparts * 4);
+        if (!cross) {        // the producer's per-tile key column sums
+            const size_t tiles = size_t((N + kPrepTile - 1) / kPrepTile);
+            p->prep_ksum = off; off = align_up(off + BH * tiles * s.d * 4);
+        }
         w.total = off;
     } catch (const std::bad_alloc&) {
         delete p;

@@ -1,0 +1,410 @@
+// The producer of the attention's inputs, fused into one kernel with the
+// statistics its bounds need.
+//
+// Source: "HeyGen 与 Google Cloud：将 Avatar IV 部署到 TPU"
+// (news.xcc.im/article/5328). "Layout Is the ABI" ¶2: the chain of small
+// operations that produces attention's inputs (normalization, rotary
+// embeddings, projections, head packing) is fused into one kernel that writes
+// exactly the layout its consumer wants. "Unchaining the Softmax" ¶2: the
+// attention's fixed max needs each query's norm and the keys' mean; this
+// kernel emits both as an epilogue, so the bounds step no longer reads Q and
+// reads K once instead of twice.
+//
+// Per token n (C = H*d channels, frame-major on an F x Hg x Wg latent grid):
+//   x_hat = x * rsqrt(mean(x^2) + eps) * gamma;   y = W x_hat  (W: [3C][C]);
+//   q, k, v = the three C-blocks of y, head h = channels [h*d, (h+1)*d);
+//   q, k turned by the 3-D rotary embedding of the token's (t, y, x);
+//   written head-packed, [B][H][N][d] bf16.
+// gamma is folded into the weights once (fsa_prep_pack_weights: W' = W*gamma),
+// and the row scale rsqrt(mean(x^2) + eps) is applied in the epilogue, which is
+// exact: (x * s * gamma) W^T = s * (x W'^T).
+//
+// gfx950 design: one workgroup of 4 waves computes a 128-token x 128-channel
+// tile (one head of q, k or v) as the transposed product Y^T = W' X^T on
+// v_mfma_f32_16x16x32_bf16, so a lane ends with one token and 4 consecutive
+// channels of each 16-channel block: rotation pairs are in-lane, and the row
+// norm reduces like the attention's row sums. W' and X tiles stream through a
+// two-stage LDS ring by direct-to-LDS copies, as the attention's K and V do.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "fsa_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kTok = fsa::kPrepTile;   // tokens per tile (4 waves x 32)
+static_assert(kTok == 128, "4 waves of 32 tokens");
+constexpr int kCh = 128;           // output channels per tile (one head of width 128)
+constexpr int kKC = 64;            // input channels per LDS chunk
+constexpr int kSub = kTok * 64;    // one [128 rows][32 columns] sub-tile, bytes
+constexpr int kTile = 2 * kSub;    // a chunk of W' or of X
+constexpr int kStage = 2 * kTile;  // W' tile, then X tile
+constexpr int kMaxPairs = 64;      // channel pairs of a head (d <= 128)
+
+struct PrepArgs {
+    const void* X;        // [B][N][C] bf16
+    const void* Wp;       // [3C][C] bf16, gamma folded in
+    void* Q;              // [B][H][N][d] bf16
+    void* K;
+    void* V;
+    float* qnorm;         // [B][H][N]: ||q|| of the bf16 outputs
+    float* ksum;          // [B][H][tiles][d]: per-tile column sums of the bf16 keys
+    int32_t B, H, N, C, T, Wg, tiles;
+    int32_t nwg;
+    float eps;
+    float freq_rev[kMaxPairs];   // rotation speed of each channel pair, revolutions per step
+};
+
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = hw & 7, s = hw >> 3;
+    return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+#define PREP_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8))
+
+__device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsigned voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
+}
+
+// Copies of input-channel chunk kc: the W' tile (128 output channels) and the
+// X tile (128 tokens), each as 2 sub-tiles of 32 columns, 8 blocks of 16 rows
+// per sub-tile; wave w copies the blocks j = 4i + w. Rows past the last token
+// repeat it (never stored). The 16-byte segment is swizzled by (row >> 1) & 3.
+__device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows,
+                                            const unsigned char* Xrows, int ntok, int C, int kc,
+                                            int wave, int lane) {
+    const int seg = lane & 3, rr = lane >> 2;
+    const unsigned sw = 16 * (seg ^ ((lane >> 3) & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * i + wave;            // block 0..15
+        const int t = j >> 3, rb = j & 7;      // sub-tile, 16-row block
+        const int row = 16 * rb + rr;
+        const unsigned col = unsigned(kc * kKC + 32 * t) * 2 + sw;
+        const unsigned dst = stage + t * kSub + rb * 1024;
+        lds_copy16(dst, Wrows, unsigned(row) * unsigned(C) * 2 + col);
+        lds_copy16(dst + kTile, Xrows, unsigned(min(row, ntok - 1)) * unsigned(C) * 2 + col);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prep_qkv(const PrepArgs p) {
+    static_assert(D == kCh, "one 128-channel head per tile");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+    __shared__ float red[4][D];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int ln = lane & 15, lj = lane >> 4;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+    // Workgroups walk (8 token tiles) x (all 3H heads) groups, so that the
+    // ones an XCD runs at once share X chunks 3H ways and W' chunks 8 ways.
+    const int L = xcd_remap(blockIdx.x, p.nwg);
+    const int H3 = 3 * p.H, per_b = p.tiles * H3;
+    const int b = L / per_b, r0 = L % per_b;
+    const int grp = r0 / (8 * H3), within = r0 % (8 * H3);
+    const int gtiles = min(8, p.tiles - 8 * grp);
+    const int col = within / gtiles, tile = 8 * grp + within % gtiles;
+    const int part = col / p.H, h = col % p.H;              // 0 q, 1 k, 2 v
+    const int tok0 = tile * kTok;
+    const int ntok = min(kTok, p.N - tok0);
+
+    const unsigned char* Wrows = static_cast<const unsigned char*>(p.Wp) + size_t(col) * D * p.C * 2;
+    const unsigned char* Xrows = static_cast<const unsigned char*>(p.X) +
+                                 (size_t(b) * p.N + tok0) * p.C * 2;
+    const int nchunks = p.C / kKC;
+    const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
+
+    f32x4 acc[2][D / 16];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) acc[g][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss[2] = {0.f, 0.f};                // sum of x^2 of this lane's token, 8 columns a step
+
+    const int ka = ln * 64 + 16 * (lj ^ ((ln >> 1) & 3));    // this lane's 16 bytes of a 16-row block
+    issue_chunk(smem_lds, Wrows, Xrows, ntok, p.C, 0, uwave, lane);
+    PREP_WAIT_VMCNT0();
+    __builtin_amdgcn_s_barrier();
+    if (nchunks > 1) issue_chunk(smem_lds + kStage, Wrows, Xrows, ntok, p.C, 1, uwave, lane);
+    int st = 0;
+    for (int kc = 0; kc < nchunks; ++kc) {
+        const unsigned char* S0 = smem + st * kStage;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 xb[2], wa[D / 16];
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                xb[g] = *reinterpret_cast<const bf16x8*>(S0 + kTile + ks * kSub +
+                                                         (32 * uwave + 16 * g) * 64 + ka);
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb)
+                wa[cb] = *reinterpret_cast<const bf16x8*>(S0 + ks * kSub + 16 * cb * 64 + ka);
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cb], xb[g], acc[g][cb], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss[g] = fmaf(float(xb[g][e]), float(xb[g][e]), ss[g]);
+        }
+        if (kc + 1 < nchunks) {
+            PREP_WAIT_VMCNT0();                          // chunk kc+1 has landed
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            if (kc + 2 < nchunks)
+                issue_chunk(smem_lds + st * kStage, Wrows, Xrows, ntok, p.C, kc + 2, uwave, lane);
+            st ^= 1;
+        }
+    }
+    PREP_WAIT_VMCNT0();
+
+    // ---- epilogue: row scale, rotation, rounding, statistics, store
+    const bool rotate = part < 2;
+    __bf16* out = static_cast<__bf16*>(part == 0 ? p.Q : part == 1 ? p.K : p.V) +
+                  (size_t(b) * p.H + h) * p.N * D;
+    float csum[D / 16][4];                   // key column sums over this lane's tokens
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) csum[cb][e] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float s2 = ss[g] + __shfl_xor(ss[g], 16, 64);
+        s2 += __shfl_xor(s2, 32, 64);
+        const float rs = 1.0f / sqrtf(s2 / float(p.C) + p.eps);
+        const int tl = 32 * uwave + 16 * g + ln;         // token within the tile
+        const bool live = tl < ntok;
+        const int n = tok0 + min(tl, ntok - 1);
+        const int f = n / p.T, pin = n % p.T;
+        const float pos[3] = {float(f), float(pin / p.Wg), float(pin % p.Wg)};
+        float qq = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = acc[g][cb][e] * rs;
+            if (rotate) {
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const int c = 16 * cb + 4 * lj + e;          // even channel of the pair
+                    const int band = c < D / 4 ? 0 : (c < D / 4 + 3 * D / 8 ? 1 : 2);
+                    const float rev = pos[band] * p.freq_rev[c >> 1];
+                    const float cs = __builtin_amdgcn_cosf(rev - floorf(rev));
+                    const float sn = __builtin_amdgcn_sinf(rev - floorf(rev));
+                    const float a = y[e], bb = y[e + 1];
+                    y[e] = a * cs - bb * sn;
+                    y[e + 1] = a * sn + bb * cs;
+                }
+            }
+            bf16x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = __bf16(y[e]);
+            if (part == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qq = fmaf(float(o4[e]), float(o4[e]), qq);
+            } else if (part == 1 && live) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) csum[cb][e] += float(o4[e]);
+            }
+            if (live) *reinterpret_cast<bf16x4*>(out + size_t(n) * D + 16 * cb + 4 * lj) = o4;
+        }
+        if (part == 0) {
+            qq += __shfl_xor(qq, 16, 64);
+            qq += __shfl_xor(qq, 32, 64);
+            if (live && lj == 0) p.qnorm[(size_t(b) * p.H + h) * p.N + n] = sqrtf(qq);
+        }
+    }
+    if (part == 1) {
+        // column sums: over the 16 tokens of each lane group, then the 4 waves
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = csum[cb][e];
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 8, 64);
+                if (ln == 0) red[uwave][16 * cb + 4 * lj + e] = v;
+            }
+        __syncthreads();
+        if (tid < D) {
+            const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+            p.ksum[((size_t(b) * p.H + h) * p.tiles + tile) * D + tid] = s;
+        }
+    }
+}
+
+// W' = W * gamma (per input channel), rounded to bf16.
+__global__ __launch_bounds__(256) void prep_fold(const __bf16* __restrict__ W,
+                                                 const float* __restrict__ gamma,
+                                                 __bf16* __restrict__ Wp, int64_t n, int C) {
+    const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    const bf16x8 w = *reinterpret_cast<const bf16x8*>(W + i);
+    bf16x8 o;
+    const int c0 = int(i % C);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __bf16(float(w[e]) * gamma[c0 + e]);
+    *reinterpret_cast<bf16x8*>(Wp + i) = o;
+}
+
+// The key mean from the producer's per-tile column sums, in tile order.
+template <int D>
+__global__ __launch_bounds__(256) void prep_mean(const float* __restrict__ ksum,
+                                                 float* __restrict__ mu, int tiles, int N) {
+    const int bh = blockIdx.x, t = threadIdx.x;
+    if (t >= D) return;
+    float s = 0.f;
+    const float* col = ksum + size_t(bh) * tiles * D + t;
+#pragma unroll 8
+    for (int i = 0; i < tiles; ++i) s += col[size_t(i) * D];
+    mu[size_t(bh) * D + t] = s / float(N);
+}
+
+// Per part (at most 256 rows of one frame): the largest ||k_j - mu|| from the
+// keys and the largest ||q_i|| from the producer's row norms.
+template <int D>
+__global__ __launch_bounds__(256) void prep_radius(const __bf16* __restrict__ K,
+                                                   const float* __restrict__ mu,
+                                                   const float* __restrict__ qnorm,
+                                                   float* __restrict__ partmax,
+                                                   float* __restrict__ partqmax, int N, int T,
+                                                   int rows_per_part, int ppf, int nparts) {
+    constexpr int LPR = D / 8;
+    constexpr int RPI = 256 / LPR;
+    __shared__ float red[RPI], qred[256];
+    const int part = blockIdx.x, bh = blockIdx.y;
+    const int frame = part / ppf, sub = part % ppf;
+    const int begin = frame * T + sub * rows_per_part;
+    const int end = min(frame * T + T, begin + rows_per_part);
+    const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+    const __bf16* Kh = K + size_t(bh) * N * D;
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = mu[size_t(bh) * D + lane * 8 + e];
+    float best = 0.f;
+    for (int r = begin + r0; r < end; r += RPI) {
+        const bf16x8 k = *reinterpret_cast<const bf16x8*>(Kh + size_t(r) * D + lane * 8);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = float(k[e]) - m[e];
+            s = fmaf(c, c, s);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+        best = fmaxf(best, sqrtf(s));
+    }
+    float qb = 0.f;
+    for (int r = begin + int(threadIdx.x); r < end; r += 256)
+        qb = fmaxf(qb, qnorm[size_t(bh) * N + r]);
+    if (lane == 0) red[r0] = best;
+    qred[threadIdx.x] = qb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = 0.f, q = 0.f;
+        for (int i = 0; i < RPI; ++i) b = fmaxf(b, red[i]);
+        for (int i = 0; i < 256; ++i) q = fmaxf(q, qred[i]);
+        partmax[size_t(bh) * nparts + part] = b;
+        partqmax[size_t(bh) * nparts + part] = q;
+    }
+}
+
+}  // namespace
+
+namespace fsa {
+
+fsa_status launch_prep_fold(const void* W, const float* gamma, void* Wp, int32_t C,
+                            hipStream_t stream) {
+    const int64_t n = int64_t(3) * C * C;
+    const int64_t blocks = (n / 8 + 255) / 256;
+    hipLaunchKernelGGL(prep_fold, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(W), gamma, static_cast<__bf16*>(Wp), n, C);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        set_error("fsa_prep_pack_weights: launch failed: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return FSA_OK;
+}
+
+fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void* Wp, void* Q,
+                       void* K, void* V, void* wsv, hipStream_t stream) {
+    const fsa_shape& s = p.shape;
+    char* ws = static_cast<char*>(wsv);
+    PrepArgs a;
+    a.X = X;
+    a.Wp = Wp;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.qnorm = reinterpret_cast<float*>(ws + p.ws.qnorm);
+    a.ksum = reinterpret_cast<float*>(ws + p.prep_ksum);
+    a.B = s.B;
+    a.H = s.H;
+    a.N = s.F * s.T;
+    a.C = s.H * s.d;
+    a.T = s.T;
+    a.Wg = Wg;
+    a.tiles = (a.N + kTok - 1) / kTok;
+    a.eps = kPrepEps;
+    // pair i of band b (n_b channels): 10000^(-2i/n_b) radians per step
+    const int bands[3] = {s.d / 4, 3 * s.d / 8, 3 * s.d / 8};
+    int pi = 0;
+    for (int bnd = 0; bnd < 3; ++bnd)
+        for (int i = 0; i < bands[bnd] / 2; ++i)
+            a.freq_rev[pi++] = float(std::pow(double(kPrepBase), -2.0 * i / bands[bnd]) /
+                                     (2.0 * 3.14159265358979323846));
+    for (; pi < kMaxPairs; ++pi) a.freq_rev[pi] = 0.f;
+    const int64_t nwg = int64_t(s.B) * a.tiles * 3 * s.H;
+    if (nwg > 0x7fffffffLL) {
+        set_error("fsa_prep: grid too large");
+        return FSA_ERR_UNSUPPORTED;
+    }
+    a.nwg = int32_t(nwg);
+    hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(256), 0, stream, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        set_error("fsa_prep: launch failed: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return FSA_OK;
+}
+
+fsa_status launch_bounds_after_prep(const fsa_plan& p, const void* K, void* wsv, float scale,
+                                    hipStream_t stream) {
+    const fsa_shape& s = p.shape;
+    char* ws = static_cast<char*>(wsv);
+    const int N = s.F * s.T, BH = s.B * s.H;
+    const int tiles = (N + kTok - 1) / kTok;
+    const Parts& q = p.bounds.q;
+    float* mu = reinterpret_cast<float*>(ws + p.ws.mu);
+    float* partmax = reinterpret_cast<float*>(ws + p.bounds.partmax);
+    float* partqmax = reinterpret_cast<float*>(ws + p.bounds.partqmax);
+    hipLaunchKernelGGL((prep_mean<128>), dim3(BH), dim3(256), 0, stream,
+                       reinterpret_cast<const float*>(ws + p.prep_ksum), mu, tiles, N);
+    hipLaunchKernelGGL((prep_radius<128>), dim3(q.count(), BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(K), mu,
+                       reinterpret_cast<const float*>(ws + p.ws.qnorm), partmax, partqmax, N, s.T,
+                       q.rows_per_part, q.per_frame, q.count());
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        set_error("fsa_bounds_after_prep: launch failed: %s", hipGetErrorString(err));
+        return FSA_ERR_HIP;
+    }
+    return launch_bounds_finalize(p, ws, scale, stream);
+}
+
+}  // namespace fsa

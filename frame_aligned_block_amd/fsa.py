@@ -47,7 +47,8 @@ EXPORTS = (
     "fsa_plan_export", "fsa_plan_valid_pairs", "fsa_plan_key_tokens", "fsa_workspace_bytes",
     "fsa_workspace_layout", "fsa_bounds", "fsa_forward", "fsa_copy_eligibility",
     "fsa_attention", "fsa_attention_workspace_bytes", "fsa_cross_attention",
-    "fsa_cross_attention_workspace_bytes",
+    "fsa_cross_attention_workspace_bytes", "fsa_prep_weight_bytes", "fsa_prep_pack_weights",
+    "fsa_prep", "fsa_bounds_after_prep",
     "fsa_cache_clear", "fsa_status_string", "fsa_last_error",
 )
 
@@ -115,6 +116,14 @@ def lib() -> ctypes.CDLL:
     L.fsa_cross_attention.restype = c_int32
     L.fsa_cross_attention_workspace_bytes.argtypes = [c_int32] * 7
     L.fsa_cross_attention_workspace_bytes.restype = c_size_t
+    L.fsa_prep_weight_bytes.argtypes = [c_int32, c_int32]
+    L.fsa_prep_weight_bytes.restype = c_size_t
+    L.fsa_prep_pack_weights.argtypes = [P, P, P, c_int32, c_int32, P]
+    L.fsa_prep_pack_weights.restype = c_int32
+    L.fsa_prep.argtypes = [P, c_int32, c_int32, P, P, P, P, P, P, P]
+    L.fsa_prep.restype = c_int32
+    L.fsa_bounds_after_prep.argtypes = [P, P, P, c_float, P]
+    L.fsa_bounds_after_prep.restype = c_int32
     L.fsa_cache_clear.argtypes = []
     L.fsa_cache_clear.restype = None
     L.fsa_status_string.argtypes = [c_int32]
@@ -295,6 +304,23 @@ def fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, dtype) -> int:
     if n == 0:
         raise FsaError(FSA_ERR_INVALID_ARG, fsa_last_error())
     return n
+
+
+def fsa_prep_weight_bytes(H: int, d: int) -> int:
+    return int(lib().fsa_prep_weight_bytes(H, d))
+
+
+def fsa_prep_pack_weights(W, gamma, Wp, H: int, d: int, stream=None) -> None:
+    _check(lib().fsa_prep_pack_weights(_ptr(W), _ptr(gamma), _ptr(Wp), H, d, _stream(stream)))
+
+
+def fsa_prep(plan: Plan, grid_h: int, grid_w: int, X, Wp, Q, K, V, ws, stream=None) -> None:
+    _check(lib().fsa_prep(plan, grid_h, grid_w, _ptr(X), _ptr(Wp), _ptr(Q), _ptr(K), _ptr(V),
+                          _ptr(ws), _stream(stream)))
+
+
+def fsa_bounds_after_prep(plan: Plan, K, ws, scale: float, stream=None) -> None:
+    _check(lib().fsa_bounds_after_prep(plan, _ptr(K), _ptr(ws), float(scale), _stream(stream)))
 
 
 def fsa_cache_clear() -> None:

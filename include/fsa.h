@@ -267,6 +267,60 @@ size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int3
 /* Drop every cached plan of fsa_attention and fsa_cross_attention. */
 void fsa_cache_clear(void);
 
+/*
+ * The producer of the attention's inputs ("Layout Is the ABI" ¶2: the chain
+ * of normalization, rotary embeddings, projections and head packing that
+ * feeds attention is fused into one kernel writing its consumer's layout).
+ * Per token n of the chunk (C = H*d channels; frame-major on a latent grid of
+ * grid_h x grid_w patches per frame, T = grid_h*grid_w):
+ *   x_hat = x / sqrt(mean_c x_c^2 + 1e-6) * gamma;  y = W x_hat;
+ *   q, k, v = channels [0,C), [C,2C), [2C,3C) of y; head h = [h*d, (h+1)*d);
+ *   q and k turned by the 3-D rotary embedding of the token's (frame t,
+ *   row y, column x): the head splits into bands of d/4 (t), 3d/8 (y) and
+ *   3d/8 (x) channels, and inside a band of n_b channels with coordinate p,
+ *   channel pair (2i, 2i+1) turns by p * 10000^(-2i/n_b) radians.
+ * The bounds' inputs come out of the same kernel: ||q_i|| of the rounded
+ * queries and per-tile column sums of the rounded keys ("Unchaining the
+ * Softmax" ¶2), so fsa_bounds_after_prep replaces fsa_bounds and no longer
+ * reads Q.
+ */
+
+/* Bytes of the packed producer weights for H heads of width d: 3*C*C bf16. */
+size_t fsa_prep_weight_bytes(int32_t H, int32_t d);
+
+/*
+ * fsa_prep_pack_weights -- fold the RMSNorm weight into the projection once:
+ * Wp[o][c] = bf16(W[o][c] * gamma[c]). W: bf16 [3C][C] (output channel major:
+ * rows [0,C) queries, [C,2C) keys, [2C,3C) values), gamma: float [C], Wp:
+ * bf16 [3C][C] (fsa_prep_weight_bytes), device memory, caller-owned, Wp not
+ * overlapping W. Errors: FSA_ERR_INVALID_ARG (NULL, misaligned, H < 1,
+ * overlap), FSA_ERR_UNSUPPORTED (d != 128), FSA_ERR_HIP.
+ */
+fsa_status fsa_prep_pack_weights(const void* W, const float* gamma, void* Wp, int32_t H,
+                                 int32_t d, hipStream_t stream);
+
+/*
+ * fsa_prep -- Q, K, V [B][H][F*T][d] bf16 of the tokens X [B][F*T][C] bf16
+ * under the packed weights Wp, for a self-attention plan of d = 128, bf16;
+ * also writes the row norms ||q_i|| (the workspace's qnorm) and the keys'
+ * per-tile column sums (private workspace) for fsa_bounds_after_prep.
+ * Outputs must not overlap each other, X, Wp or ws. Errors:
+ * FSA_ERR_INVALID_ARG (NULL, misaligned, overlap, grid_h*grid_w != T),
+ * FSA_ERR_UNSUPPORTED (a cross plan, d != 128 or not bf16),
+ * FSA_ERR_WORKSPACE, FSA_ERR_HIP.
+ */
+fsa_status fsa_prep(const fsa_plan* plan, int32_t grid_h, int32_t grid_w, const void* X,
+                    const void* Wp, void* Q, void* K, void* V, void* ws, hipStream_t stream);
+
+/*
+ * fsa_bounds_after_prep -- what fsa_bounds computes (mu, radii, statistics,
+ * flags in ws), from the statistics fsa_prep left in ws and one read of K.
+ * Call it after fsa_prep on the same plan, K and workspace; then fsa_forward.
+ * Errors as fsa_bounds, and FSA_ERR_UNSUPPORTED as fsa_prep.
+ */
+fsa_status fsa_bounds_after_prep(const fsa_plan* plan, const void* K, void* ws, float scale,
+                                 hipStream_t stream);
+
 const char* fsa_status_string(fsa_status status);
 /* Detail of the calling thread's last failed call ("" if none). */
 const char* fsa_last_error(void);

@@ -92,6 +92,23 @@ def apply_rope(U, angles) -> np.ndarray:
     return out
 
 
+def prep_rows(X, W, gamma, F: int, Hg: int, Wg: int, H: int, d: int, b: int, rows,
+              eps: float = EPS, base: float = BASE):
+    """Q, K, V [H, len(rows), d] of the tokens ``rows`` of batch b: every step
+    of the chain is per token, so a subset of tokens is computed alone."""
+    rows = np.asarray(rows, dtype=np.int64)
+    C = H * d
+    x = _f64(X[b][rows])
+    y = rms_norm(x, gamma, eps) @ _f64(W).T                      # [n, 3C]
+    ang = rope_angles(token_coords(F, Hg, Wg)[rows], d, base)
+    def head(part, h):
+        return y[:, part * C + h * d:part * C + (h + 1) * d]
+    Q = np.stack([apply_rope(head(0, h), ang) for h in range(H)])
+    K = np.stack([apply_rope(head(1, h), ang) for h in range(H)])
+    V = np.stack([head(2, h) for h in range(H)])
+    return Q, K, V
+
+
 def prep(X, W, gamma, F: int, Hg: int, Wg: int, H: int, d: int,
          eps: float = EPS, base: float = BASE):
     """Q, K, V [B, H, N, d] (float64) from tokens X [B, N, C], C = H*d.
@@ -102,9 +119,6 @@ def prep(X, W, gamma, F: int, Hg: int, Wg: int, H: int, d: int,
     X = _f64(X)
     B, N, C = X.shape
     assert C == H * d and N == F * Hg * Wg
-    Y = rms_norm(X, gamma, eps) @ _f64(W).T                     # [B, N, 3C]
-    def pack(part):
-        return Y[:, :, part * C:(part + 1) * C].reshape(B, N, H, d).transpose(0, 2, 1, 3)
-    Q, K, V = pack(0), pack(1), pack(2)
-    ang = rope_angles(token_coords(F, Hg, Wg), d, base)
-    return apply_rope(Q, ang), apply_rope(K, ang), V
+    out = [prep_rows(X, W, gamma, F, Hg, Wg, H, d, b, np.arange(N), eps, base)
+           for b in range(B)]
+    return tuple(np.stack([o[i] for o in out]) for i in range(3))

@@ -183,3 +183,46 @@ def test_cross_attention_validates_before_launch():
     with pytest.raises(fsa.FsaError):
         fsa.fsa_cross_attention_workspace_bytes(F, T, 0, B, H, d, fsa.FSA_F32)
     fsa.fsa_cache_clear()
+
+
+def test_prep_validates_before_launch():
+    F, T, H, d = 3, 48, 2, 128
+    p = fsa.fsa_plan_create(fsa.make_shape(1, H, F, T, d, 1, 0, 0, 0, fsa.FSA_BF16))
+    nb = 1 * H * F * T * d * 2
+    wb = fsa.fsa_prep_weight_bytes(H, d)
+    assert wb == 3 * (H * d) ** 2 * 2
+    X, Wp, Q, K, V, ws = (FAKE * (1 << i) for i in range(6, 12))
+    ok = dict(grid_h=4, grid_w=12, X=X, Wp=Wp, Q=Q, K=K, V=V, ws=ws)
+
+    def call(plan=p, **over):
+        a = dict(ok)
+        a.update(over)
+        fsa.fsa_prep(plan, a["grid_h"], a["grid_w"], a["X"], a["Wp"], a["Q"], a["K"], a["V"],
+                     a["ws"], stream=0)
+    cross = fsa.fsa_plan_create_cross(fsa.make_shape(1, H, F, T, d, 0, 0, 0, 0, fsa.FSA_BF16), 64)
+    d64 = fsa.fsa_plan_create(fsa.make_shape(1, H, F, T, 64, 1, 0, 0, 0, fsa.FSA_BF16))
+    for over, status in [
+        (dict(grid_w=10), fsa.FSA_ERR_INVALID_ARG),          # 4 x 10 != 48
+        (dict(X=None), fsa.FSA_ERR_INVALID_ARG),
+        (dict(Q=Q + 8), fsa.FSA_ERR_INVALID_ARG),             # misaligned
+        (dict(K=Q + nb // 2), fsa.FSA_ERR_INVALID_ARG),       # K overlaps Q
+        (dict(V=X), fsa.FSA_ERR_INVALID_ARG),                 # V overlaps X
+        (dict(ws=None), fsa.FSA_ERR_WORKSPACE),
+        (dict(plan=cross), fsa.FSA_ERR_UNSUPPORTED),
+        (dict(plan=d64), fsa.FSA_ERR_UNSUPPORTED),
+    ]:
+        with pytest.raises(fsa.FsaError) as e:
+            call(**over)
+        assert e.value.status == status, (over, fsa.fsa_last_error())
+    for fn, status in [
+        (lambda: fsa.fsa_bounds_after_prep(p, None, ws, 0.1, stream=0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds_after_prep(p, K, ws, 0.0, stream=0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_bounds_after_prep(p, K, ws + 16, 0.1, stream=0), fsa.FSA_ERR_WORKSPACE),
+        (lambda: fsa.fsa_bounds_after_prep(cross, K, ws, 0.1, stream=0), fsa.FSA_ERR_UNSUPPORTED),
+        (lambda: fsa.fsa_prep_pack_weights(None, FAKE, Wp, H, d, stream=0), fsa.FSA_ERR_INVALID_ARG),
+        (lambda: fsa.fsa_prep_pack_weights(X, FAKE, Wp, H, 64, stream=0), fsa.FSA_ERR_UNSUPPORTED),
+        (lambda: fsa.fsa_prep_pack_weights(X, FAKE, X + 64, H, d, stream=0), fsa.FSA_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(fsa.FsaError) as e:
+            fn()
+        assert e.value.status == status, fsa.fsa_last_error()
