@@ -85,7 +85,7 @@ namespace fsa {
 constexpr float kPrepEps = 1e-6f;
 constexpr double kPrepBase = 10000.0;
 // Tokens per producer tile (the key column sums are kept per tile).
-constexpr int kPrepTile = 128;
+constexpr int kPrepTile = 256;
 
 // Thread-local last-error text (abi.cpp).
 void set_error(const char* fmt, ...);

@@ -19,12 +19,14 @@
 // and the row scale rsqrt(mean(x^2) + eps) is applied in the epilogue, which is
 // exact: (x * s * gamma) W^T = s * (x W'^T).
 //
-// gfx950 design: one workgroup of 4 waves computes a 128-token x 128-channel
-// tile (one head of q, k or v) as the transposed product Y^T = W' X^T on
-// v_mfma_f32_16x16x32_bf16, so a lane ends with one token and 4 consecutive
-// channels of each 16-channel block: rotation pairs are in-lane, and the row
-// norm reduces like the attention's row sums. W' and X tiles stream through a
-// two-stage LDS ring by direct-to-LDS copies, as the attention's K and V do.
+// gfx950 design: one workgroup of 4 waves (two workgroups per CU, so two
+// waves per SIMD) computes a 256-token x 128-channel tile (one head of q, k or
+// v) as the transposed product Y^T = W' X^T on v_mfma_f32_16x16x32_bf16; each
+// wave owns 64 tokens of the head, so a lane ends with 4 tokens and 4
+// consecutive channels of each 16-channel block: rotation pairs are in-lane,
+// and the row norm reduces like the attention's row sums. W' and X tiles
+// stream through a two-stage LDS ring of 32-channel chunks (2 x 24 KB) by
+// direct-to-LDS copies, as the attention's K and V do.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -38,14 +40,23 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTok = fsa::kPrepTile;   // tokens per tile (4 waves x 32)
-static_assert(kTok == 128, "4 waves of 32 tokens");
-constexpr int kCh = 128;           // output channels per tile (one head of width 128)
-constexpr int kKC = 64;            // input channels per LDS chunk
-constexpr int kSub = kTok * 64;    // one [128 rows][32 columns] sub-tile, bytes
-constexpr int kTile = 2 * kSub;    // a chunk of W' or of X
-constexpr int kStage = 2 * kTile;  // W' tile, then X tile
-constexpr int kMaxPairs = 64;      // channel pairs of a head (d <= 128)
+constexpr int kWaves = 4;                 // two workgroups (two waves per SIMD) per CU
+constexpr int kTG = 64;                   // tokens per wave (4 granules of 16)
+constexpr int kTok = fsa::kPrepTile;      // tokens per tile: 4 wave rows of 64
+static_assert(kTok == 4 * kTG, "4 rows of waves");
+constexpr int kCh = 128;                  // output channels per wave: one head of width 128
+constexpr int kCols = kWaves / 4;         // heads per workgroup (one wave column of 4)
+constexpr int kRows = kCols * kCh;        // W' rows of a tile
+constexpr int kKC = 32;                   // input channels per LDS chunk (one k-step)
+constexpr int kSubs = kKC / 32;           // 32-column sub-tiles per chunk
+constexpr int kWSub = kRows * 64;         // a [256 rows][32 columns] sub-tile of W', bytes
+constexpr int kXSub = kTok * 64;          // the same for X
+constexpr int kWTile = kSubs * kWSub;
+constexpr int kStage = kWTile + kSubs * kXSub;
+// Direct-to-LDS copies address LDS through the low 16 bits of M0: the ring
+// must sit in the first 64 KB.
+static_assert(2 * kStage <= 65536, "copy ring within the first 64 KB of LDS");
+constexpr int kMaxPairs = 64;             // channel pairs of a head (d <= 128)
 
 struct PrepArgs {
     const void* X;        // [B][N][C] bf16
@@ -55,7 +66,7 @@ struct PrepArgs {
     void* V;
     float* qnorm;         // [B][H][N]: ||q|| of the bf16 outputs
     float* ksum;          // [B][H][tiles][d]: per-tile column sums of the bf16 keys
-    int32_t B, H, N, C, T, Wg, tiles;
+    int32_t B, H, N, C, T, Wg, tiles, pairs;
     int32_t nwg;
     float eps;
     float freq_rev[kMaxPairs];   // rotation speed of each channel pair, revolutions per step
@@ -74,87 +85,110 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
                  :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Copies of input-channel chunk kc: the W' tile (128 output channels) and the
-// X tile (128 tokens), each as 2 sub-tiles of 32 columns, 8 blocks of 16 rows
-// per sub-tile; wave w copies the blocks j = 4i + w. Rows past the last token
-// repeat it (never stored). The 16-byte segment is swizzled by (row >> 1) & 3.
-__device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows,
+// Copies of input-channel chunk kc: the W' tile (the head's 128 output
+// channels) and the X tile (256 tokens, rows past the last repeat it; never
+// stored), as sub-tiles of 32 columns in blocks of 16 rows; wave w copies the
+// blocks j = 4i + w. The 16-byte segment is swizzled by (row >> 1) & 3.
+// (Workgroups stay at 4 waves: in 8-wave workgroups, direct-to-LDS copies to
+// some destinations were measured not to land.)
+constexpr int kCopyWaves = 4;
+
+__device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows, int nwrows,
                                             const unsigned char* Xrows, int ntok, int C, int kc,
                                             int wave, int lane) {
+    if (wave >= kCopyWaves) return;
     const int seg = lane & 3, rr = lane >> 2;
     const unsigned sw = 16 * (seg ^ ((lane >> 3) & 3));
+    constexpr int WB = kSubs * kRows / 16, XB = kSubs * kTok / 16;   // 16-row blocks
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = 4 * i + wave;            // block 0..15
-        const int t = j >> 3, rb = j & 7;      // sub-tile, 16-row block
-        const int row = 16 * rb + rr;
+    for (int i = 0; i < WB / kCopyWaves; ++i) {
+        const int j = kCopyWaves * i + wave;
+        const int t = j / (kRows / 16), rb = j % (kRows / 16);
         const unsigned col = unsigned(kc * kKC + 32 * t) * 2 + sw;
-        const unsigned dst = stage + t * kSub + rb * 1024;
-        lds_copy16(dst, Wrows, unsigned(row) * unsigned(C) * 2 + col);
-        lds_copy16(dst + kTile, Xrows, unsigned(min(row, ntok - 1)) * unsigned(C) * 2 + col);
+        const int wrow = min(16 * rb + rr, nwrows - 1);
+        lds_copy16(stage + t * kWSub + rb * 1024, Wrows, unsigned(wrow) * unsigned(C) * 2 + col);
+    }
+#pragma unroll
+    for (int i = 0; i < XB / kCopyWaves; ++i) {
+        const int j = kCopyWaves * i + wave;
+        const int t = j / (kTok / 16), rb = j % (kTok / 16);
+        const unsigned col = unsigned(kc * kKC + 32 * t) * 2 + sw;
+        const int xrow = min(16 * rb + rr, ntok - 1);
+        lds_copy16(stage + kWTile + t * kXSub + rb * 1024, Xrows,
+                   unsigned(xrow) * unsigned(C) * 2 + col);
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prep_qkv(const PrepArgs p) {
-    static_assert(D == kCh, "one 128-channel head per tile");
+__global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
+    static_assert(D == kCh, "one 128-channel head per wave column");
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
-    __shared__ float red[4][D];
+    __shared__ float red[kWaves][D];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int wr = uwave & 3, wc = uwave >> 2;             // wave row (tokens), column (head)
 
-    // Workgroups walk (8 token tiles) x (all 3H heads) groups, so that the
-    // ones an XCD runs at once share X chunks 3H ways and W' chunks 8 ways.
+    // Workgroups walk (8 token tiles) x (all head pairs) groups, so that the
+    // ones an XCD runs at once share X chunks and W' chunks.
     const int L = xcd_remap(blockIdx.x, p.nwg);
-    const int H3 = 3 * p.H, per_b = p.tiles * H3;
+    const int per_b = p.tiles * p.pairs;
     const int b = L / per_b, r0 = L % per_b;
-    const int grp = r0 / (8 * H3), within = r0 % (8 * H3);
+    const int grp = r0 / (8 * p.pairs), within = r0 % (8 * p.pairs);
     const int gtiles = min(8, p.tiles - 8 * grp);
-    const int col = within / gtiles, tile = 8 * grp + within % gtiles;
-    const int part = col / p.H, h = col % p.H;              // 0 q, 1 k, 2 v
+    const int pair = within / gtiles, tile = 8 * grp + within % gtiles;
+    const int ncols = 3 * p.H;
+    const int col0 = kCols * pair;
+    const int col = min(col0 + wc, ncols - 1);              // this wave column's head
+    const bool col_live = col0 + wc < ncols;                // uniform per wave
+    const int part = col / p.H, h = col % p.H;               // 0 q, 1 k, 2 v
     const int tok0 = tile * kTok;
     const int ntok = min(kTok, p.N - tok0);
 
-    const unsigned char* Wrows = static_cast<const unsigned char*>(p.Wp) + size_t(col) * D * p.C * 2;
+    const unsigned char* Wrows = static_cast<const unsigned char*>(p.Wp) + size_t(col0) * D * p.C * 2;
+    const int nwrows = min(kRows, (ncols - col0) * D);
     const unsigned char* Xrows = static_cast<const unsigned char*>(p.X) +
                                  (size_t(b) * p.N + tok0) * p.C * 2;
     const int nchunks = p.C / kKC;
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
 
-    f32x4 acc[2][D / 16];
+    constexpr int G = kTG / 16;
+    f32x4 acc[G][D / 16];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb) acc[g][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss[2] = {0.f, 0.f};                // sum of x^2 of this lane's token, 8 columns a step
+    float ss[G];                             // sum of x^2 of this lane's tokens
+#pragma unroll
+    for (int g = 0; g < G; ++g) ss[g] = 0.f;
 
     const int ka = ln * 64 + 16 * (lj ^ ((ln >> 1) & 3));    // this lane's 16 bytes of a 16-row block
-    issue_chunk(smem_lds, Wrows, Xrows, ntok, p.C, 0, uwave, lane);
+    issue_chunk(smem_lds, Wrows, nwrows, Xrows, ntok, p.C, 0, uwave, lane);
     PREP_WAIT_VMCNT0();
     __builtin_amdgcn_s_barrier();
-    if (nchunks > 1) issue_chunk(smem_lds + kStage, Wrows, Xrows, ntok, p.C, 1, uwave, lane);
+    if (nchunks > 1) issue_chunk(smem_lds + kStage, Wrows, nwrows, Xrows, ntok, p.C, 1, uwave, lane);
     int st = 0;
     for (int kc = 0; kc < nchunks; ++kc) {
         const unsigned char* S0 = smem + st * kStage;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 xb[2], wa[D / 16];
+        for (int ks = 0; ks < kSubs; ++ks) {
+            bf16x8 xb[G], wa[D / 16];
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
-                xb[g] = *reinterpret_cast<const bf16x8*>(S0 + kTile + ks * kSub +
-                                                         (32 * uwave + 16 * g) * 64 + ka);
-#pragma unroll
-            for (int cb = 0; cb < D / 16; ++cb)
-                wa[cb] = *reinterpret_cast<const bf16x8*>(S0 + ks * kSub + 16 * cb * 64 + ka);
+            for (int g = 0; g < G; ++g)
+                xb[g] = *reinterpret_cast<const bf16x8*>(S0 + kWTile + ks * kXSub +
+                                                         (kTG * wr + 16 * g) * 64 + ka);
 #pragma unroll
             for (int cb = 0; cb < D / 16; ++cb)
+                wa[cb] = *reinterpret_cast<const bf16x8*>(S0 + ks * kWSub +
+                                                          (kCh * wc + 16 * cb) * 64 + ka);
 #pragma unroll
-                for (int g = 0; g < 2; ++g)
+            for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
                     acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cb], xb[g], acc[g][cb], 0, 0, 0);
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+            for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss[g] = fmaf(float(xb[g][e]), float(xb[g][e]), ss[g]);
         }
@@ -163,7 +197,8 @@ __global__ __launch_bounds__(256, 2) void prep_qkv(const PrepArgs p) {
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));   // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             if (kc + 2 < nchunks)
-                issue_chunk(smem_lds + st * kStage, Wrows, Xrows, ntok, p.C, kc + 2, uwave, lane);
+                issue_chunk(smem_lds + st * kStage, Wrows, nwrows, Xrows, ntok, p.C, kc + 2, uwave,
+                            lane);
             st ^= 1;
         }
     }
@@ -179,12 +214,12 @@ __global__ __launch_bounds__(256, 2) void prep_qkv(const PrepArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) csum[cb][e] = 0.f;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
         float s2 = ss[g] + __shfl_xor(ss[g], 16, 64);
         s2 += __shfl_xor(s2, 32, 64);
         const float rs = 1.0f / sqrtf(s2 / float(p.C) + p.eps);
-        const int tl = 32 * uwave + 16 * g + ln;         // token within the tile
-        const bool live = tl < ntok;
+        const int tl = kTG * wr + 16 * g + ln;           // token within the tile
+        const bool live = col_live && tl < ntok;
         const int n = tok0 + min(tl, ntok - 1);
         const int f = n / p.T, pin = n % p.T;
         const float pos[3] = {float(f), float(pin / p.Wg), float(pin % p.Wg)};
@@ -225,23 +260,25 @@ __global__ __launch_bounds__(256, 2) void prep_qkv(const PrepArgs p) {
             if (live && lj == 0) p.qnorm[(size_t(b) * p.H + h) * p.N + n] = sqrtf(qq);
         }
     }
-    if (part == 1) {
-        // column sums: over the 16 tokens of each lane group, then the 4 waves
+    // key column sums: over the 16 tokens of each lane group, then the 4 wave
+    // rows of the column, in order (every wave passes the same barrier)
 #pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb)
+    for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = csum[cb][e];
-                v += __shfl_xor(v, 1, 64);
-                v += __shfl_xor(v, 2, 64);
-                v += __shfl_xor(v, 4, 64);
-                v += __shfl_xor(v, 8, 64);
-                if (ln == 0) red[uwave][16 * cb + 4 * lj + e] = v;
-            }
-        __syncthreads();
-        if (tid < D) {
-            const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-            p.ksum[((size_t(b) * p.H + h) * p.tiles + tile) * D + tid] = s;
+        for (int e = 0; e < 4; ++e) {
+            float v = csum[cb][e];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            if (ln == 0) red[uwave][16 * cb + 4 * lj + e] = v;
+        }
+    __syncthreads();
+    if (part == 1 && col_live && wr == 0) {
+        for (int c = lane; c < D; c += 64) {
+            const float s = ((red[4 * wc][c] + red[4 * wc + 1][c]) + red[4 * wc + 2][c]) +
+                            red[4 * wc + 3][c];
+            p.ksum[((size_t(b) * p.H + h) * p.tiles + tile) * D + c] = s;
         }
     }
 }
@@ -359,6 +396,7 @@ fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void*
     a.T = s.T;
     a.Wg = Wg;
     a.tiles = (a.N + kTok - 1) / kTok;
+    a.pairs = (3 * s.H + kCols - 1) / kCols;
     a.eps = kPrepEps;
     // pair i of band b (n_b channels): 10000^(-2i/n_b) radians per step
     const int bands[3] = {s.d / 4, 3 * s.d / 8, 3 * s.d / 8};
@@ -368,13 +406,13 @@ fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void*
             a.freq_rev[pi++] = float(std::pow(double(kPrepBase), -2.0 * i / bands[bnd]) /
                                      (2.0 * 3.14159265358979323846));
     for (; pi < kMaxPairs; ++pi) a.freq_rev[pi] = 0.f;
-    const int64_t nwg = int64_t(s.B) * a.tiles * 3 * s.H;
+    const int64_t nwg = int64_t(s.B) * a.tiles * a.pairs;
     if (nwg > 0x7fffffffLL) {
         set_error("fsa_prep: grid too large");
         return FSA_ERR_UNSUPPORTED;
     }
     a.nwg = int32_t(nwg);
-    hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(kWaves * 64), 0, stream, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         set_error("fsa_prep: launch failed: %s", hipGetErrorString(err));
