@@ -17,9 +17,12 @@ regenerated without drawing the others):
       c = 4 * N(0,1) [1, d]        (only when keys carry a shared mean);
       v = N(0,1) [N, d];
       p = randint(0, T) [F]        (only for a loose head);
-  * k = e + c  (or k = e);
+      u = randint(0, T - R + 1) [F] (only for configs with R = hot_rows > 0);
+  * k = sigma * e + c  (or k = sigma * e), sigma = key_sigma (1 by default);
   * a loose head multiplies, in every frame g (or only in the frames a config
     lists), the raw key at token g*T + p[g] (shared mean included) by 20;
+  * with hot rows, the queries at tokens g*T + u[g] + [0, R) of every frame g
+    are multiplied by hot_scale;
   * finally q, k, v are cast to the config dtype (bf16 rounds to nearest even).
 The cast tensors are the inputs; the oracle upcasts exactly these values.
 
@@ -51,6 +54,9 @@ class Config:
     B: int = 1
     M: int = 0        # cross-attention: reference tokens every query attends to (0 = self)
     grid: tuple = ()  # (Hg, Wg) latent patch grid of a frame (T = Hg*Wg); producer workloads
+    key_sigma: float = 1.0  # spread of the keys around their shared mean
+    hot_rows: int = 0       # a band of this many query rows per frame is scaled ...
+    hot_scale: float = 1.0  # ... by this factor
 
     @property
     def N(self) -> int:
@@ -107,6 +113,17 @@ CONFIGS = {
     "xref-small": Config("xref-small", F=4, T=880, H=4, d=128, dtype="bf16", window=0,
                          ref_frame=0, shared_mean=True, M=720, loose_period=4,
                          loose_phase=3),
+    # Looser heads: keys spread twice as wide (every head's largest row bound
+    # is above the per-head threshold, so the per-head and per-frame checks
+    # send everything online) and, in every frame, a band of 256 query rows
+    # with 2.5x the norm. Only the rows of that band have a gap bound too
+    # loose for the fixed max: the case for the per-row-block check.
+    "loose-rows": Config("loose-rows", F=13, T=3600, H=24, d=128, dtype="bf16", window=2,
+                         ref_frame=0, shared_mean=True, key_sigma=2.0, hot_rows=256,
+                         hot_scale=2.5),
+    "loose-rows-small": Config("loose-rows-small", F=5, T=880, H=4, d=128, dtype="bf16",
+                               window=2, ref_frame=0, shared_mean=True, key_sigma=2.0,
+                               hot_rows=160, hot_scale=2.5),
     # Producer workloads: the tokens of a chunk (C = H*d channels) go through
     # RMSNorm, the Q/K/V projection, 3-D rotary embedding and head packing
     # into the attention's layout. The 720p one is the SR transformer layer
@@ -131,6 +148,8 @@ def make_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
     kw = dict(generator=g, device=device, dtype=torch.float32)
     q = torch.randn((N, d), **kw)
     k = torch.randn((N, d), **kw)
+    if cfg.key_sigma != 1.0:
+        k *= cfg.key_sigma
     if cfg.shared_mean:
         k += 4.0 * torch.randn((1, d), **kw)
     v = torch.randn((N, d), **kw)
@@ -140,6 +159,11 @@ def make_head(cfg: Config, seed: int, b: int, h: int, device="cpu"):
         if cfg.loose_frames:
             rows = rows[list(cfg.loose_frames)]
         k[rows] *= 20.0
+    if cfg.hot_rows:
+        u = torch.randint(0, cfg.T - cfg.hot_rows + 1, (cfg.F,), generator=g, device=device)
+        rows = (torch.arange(cfg.F, device=device) * cfg.T + u)[:, None] \
+            + torch.arange(cfg.hot_rows, device=device)[None, :]
+        q[rows.reshape(-1)] *= cfg.hot_scale
     dt = cfg.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)
 

@@ -27,7 +27,11 @@ Readings of points the page leaves open (each is listed in the design notes):
   * no causal masking inside a frame;
   * the key mean is one vector per (batch, head), over all N keys;
   * eligibility of a head: max over its rows of the Cauchy-Schwarz bound
-    scale * ||q_i|| * max_{j in slice} ||k_j - mu|| is at most BETA = 32.
+    scale * ||q_i|| * max_{j in slice} ||k_j - mu|| is at most BETA = 32;
+  * the finer, tighter check per row: the fixed max exceeds the row's true
+    maximum by at most the gap bound G_i = B_i - scale <q_i, mean_S(k) - mu>
+    (a maximum is at least the mean), and a row may take the fixed max when
+    G_i <= GAP_LIMIT = 2 * BETA, the largest gap the per-head check allows.
 
 Precision: every function upcasts its inputs to float64 and computes in
 float64 with numpy; matrix products are numpy's.
@@ -47,6 +51,11 @@ import numpy as np
 # Threshold on the per-head bound statistic (logit units). A head whose largest
 # per-row bound exceeds it uses the online softmax path.
 BETA = 32.0
+
+# Limit on a row's gap bound (logit units): the per-head check bounds the gap
+# by 2 * BETA (the logits of a row lie within +-B_i), so a row whose own gap
+# bound is at most this keeps the same guarantee.
+GAP_LIMIT = 2.0 * BETA
 
 # Query rows processed together in one numpy product (memory bound, not math).
 ROW_CHUNK = 512
@@ -178,6 +187,39 @@ def bounds(Q, K, F: int, T: int, window: int, ref_frame: int, scale: float,
     return {"mu": mu, "qnorm": qnorm, "R": R, "R_S": R_S, "bound": bound,
             "stat": stat, "elig": stat <= beta,
             "stat_frame": stat_frame, "elig_frame": stat_frame <= beta}
+
+
+def gap_bounds(Q, K, F: int, T: int, window: int, ref_frame: int, scale: float,
+               limit: float = GAP_LIMIT) -> dict:
+    """Per-row bound on how far the fixed max lies above the row's true max.
+
+    In the centred frame ("Unchaining the Softmax" ¶2) the fixed max of row i
+    is its Cauchy-Schwarz bound B_i, and the row's largest logit is at least
+    the mean of its logits over the slice ("Unchaining the Softmax" ¶3: each
+    row sees its own slice), scale <q_i, kbar_S - mu> with kbar_S the mean
+    key of the slice S(f(i)). So
+        B_i - max_j scale <q_i, k_j - mu>  <=  G_i = B_i - scale <q_i, kbar_S - mu>,
+    and 0 <= G_i <= 2 B_i. A row whose G_i is at most ``limit`` may take the
+    fixed max with the guarantee the per-head check gives (its largest term
+    is at least exp(-limit)).
+
+    Returns dslice [B,H,F,d] (kbar_S(f) - mu), bound [B,H,N] (B_i), gap
+    [B,H,N] (G_i) and ok [B,H,N] (G_i <= limit).
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    B, H, N, d = K.shape
+    assert N == F * T
+    cs = bounds(Q, K, F, T, window, ref_frame, scale)
+    mu = cs["mu"]
+    frame_mean = K.reshape(B, H, F, T, d).mean(axis=3)          # [B,H,F,d]
+    dslice = np.empty((B, H, F, d))
+    for f in range(F):
+        dslice[:, :, f] = frame_mean[:, :, slice_frames(F, window, ref_frame, f)].mean(axis=2) - mu
+    frame_of_row = np.arange(N) // T
+    lower = scale * np.einsum("bhnd,bhnd->bhn", Q, dslice[:, :, frame_of_row])
+    gap = cs["bound"] - lower
+    return {"dslice": dslice, "bound": cs["bound"], "gap": gap, "ok": gap <= limit}
 
 
 # --------------------------------------------------------------------------
@@ -370,8 +412,10 @@ def cross_bounds(Q, Kr, F: int, T: int, scale: float, beta: float = BETA) -> dic
     scale ||q_i|| R with R = max_j ||kr_j - mu|| ("Unchaining the Softmax"
     ¶2-¶3). Eligibility per head (stat = max_i bound_i <= beta) and per query
     frame (stat_frame over the frame's rows), as for self-attention.
+    Every row's slice is the whole reference set, whose mean is mu, so the
+    row's gap bound (see gap_bounds) is its bound itself.
     Returns mu [B,H,d], qnorm [B,H,N], R [B,H], bound [B,H,N], stat, elig,
-    stat_frame [B,H,F], elig_frame."""
+    stat_frame [B,H,F], elig_frame, gap [B,H,N] (= bound)."""
     Q = _f64(Q)
     Kr = _f64(Kr)
     B, H, N, d = Q.shape
@@ -385,4 +429,4 @@ def cross_bounds(Q, Kr, F: int, T: int, scale: float, beta: float = BETA) -> dic
     stat_frame = bound.reshape(B, H, F, T).max(axis=-1)
     return {"mu": mu, "qnorm": qnorm, "R": R, "bound": bound, "stat": stat,
             "elig": stat <= beta, "stat_frame": stat_frame,
-            "elig_frame": stat_frame <= beta}
+            "elig_frame": stat_frame <= beta, "gap": bound.copy()}

@@ -306,6 +306,106 @@ def test_frame_eligibility_follows_the_outlier_frame():
         assert bool(b["elig"][0, 0]) == bool(b["elig_frame"][0, 0].all())
 
 
+# ---------------------------------------------------------------- gap bound
+
+def test_gap_bound_hand_case():
+    """A case small enough to work out on paper (d = 2, scale 1, F = 2 frames
+    of T = 2 tokens, window 0, reference frame 0, so S(0) = {0} and
+    S(1) = {0, 1}). Keys: frame 0 (1,0), (3,0); frame 1 (-1,0), (-3,0); their
+    mean is 0, every frame's largest norm is 3, the slice means are (2,0) and
+    (0,0). Rows q = (1,0), (-1,0) in frame 0 and (1,0), (0,2) in frame 1 have
+    bounds 3, 3, 3, 6 and gap bounds 3-2 = 1, 3+2 = 5, 3, 6. Their true gaps
+    (bound minus the largest logit) are 0, 4, 0 and 6: the last row scores
+    every key 0, so its bound is tight."""
+    K = np.array([[1.0, 0.0], [3.0, 0.0], [-1.0, 0.0], [-3.0, 0.0]])[None, None]
+    Q = np.array([[1.0, 0.0], [-1.0, 0.0], [1.0, 0.0], [0.0, 2.0]])[None, None]
+    g = orc.gap_bounds(Q, K, 2, 2, 0, 0, 1.0)
+    assert np.allclose(g["bound"][0, 0], [3, 3, 3, 6], rtol=0, atol=1e-15)
+    assert np.allclose(g["gap"][0, 0], [1, 5, 3, 6], rtol=0, atol=1e-15)
+    assert np.allclose(g["dslice"][0, 0], [[2, 0], [0, 0]], rtol=0, atol=1e-15)
+    true_gap = np.array([3 - 3, 3 - (-1), 3 - 3, 6 - 0])
+    assert np.all(g["gap"][0, 0] >= true_gap)
+    assert g["ok"][0, 0].all() and not orc.gap_bounds(Q, K, 2, 2, 0, 0, 1.0, limit=5.5)["ok"][0, 0, 3]
+
+
+@pytest.mark.parametrize("name", ["tiny", "loose-rows-small", "stress"])
+def test_gap_bound_brackets_the_true_gap(name):
+    """For every row (sampled rows at the 720p shape), brute force in fp64:
+    B_i - max_j scale <q_i, k_j - mu> <= G_i <= 2 B_i, the upper end by
+    Cauchy-Schwarz on the slice mean. Head 7 of stress is its loose head."""
+    cfg = CONFIGS[name]
+    h = 7 if name == "stress" else 1
+    q, k, _ = make_head(cfg, 0, 0, h)
+    Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+    g = orc.gap_bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    rng = np.random.default_rng(3)
+    rows = np.arange(cfg.N) if cfg.N <= 5000 else rng.choice(cfg.N, 400, replace=False)
+    mu = K[0, 0].mean(axis=0)
+    for i in rows:
+        keys = orc.slice_keys(cfg.F, cfg.T, cfg.window, cfg.ref_frame, int(i) // cfg.T)
+        true_max = (cfg.scale * ((K[0, 0, keys] - mu) @ Q[0, 0, i])).max()
+        true_gap = g["bound"][0, 0, i] - true_max
+        assert true_gap <= g["gap"][0, 0, i] * (1 + 1e-12) + 1e-12, (i, true_gap, g["gap"][0, 0, i])
+        assert g["gap"][0, 0, i] <= 2 * g["bound"][0, 0, i] * (1 + 1e-12), i
+
+
+def test_gap_bound_invariances():
+    """Moving every key by one vector changes neither the slice offsets nor the
+    gap bounds (they are taken from centred keys); a window that covers every
+    frame makes each slice the whole chunk, whose mean is mu, so G_i = B_i."""
+    rng = np.random.default_rng(5)
+    F, T, d = 5, 16, 8
+    Q, K, _ = rand_qkv(rng, 1, 2, F * T, d, mean_scale=2.0)
+    a = orc.gap_bounds(Q, K, F, T, 1, 0, 0.4)
+    b = orc.gap_bounds(Q, K + rng.standard_normal((1, 2, 1, d)) * 5.0, F, T, 1, 0, 0.4)
+    assert np.allclose(a["gap"], b["gap"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(a["dslice"], b["dslice"], rtol=1e-12, atol=1e-12)
+    full = orc.gap_bounds(Q, K, F, T, F - 1, 0, 0.4)
+    assert np.allclose(full["dslice"], 0.0, atol=1e-13)
+    assert np.allclose(full["gap"], full["bound"], rtol=1e-13)
+
+
+@pytest.mark.parametrize("name", ["loose-rows-small", "loose-rows"])
+def test_gap_rows_by_construction(name):
+    """The looser workloads: every head's largest bound is far above BETA (the
+    per-head and per-frame checks fail everywhere), yet every row outside a
+    frame's hot band has a gap bound well within GAP_LIMIT, and every frame's
+    hot band holds rows well beyond it."""
+    cfg = CONFIGS[name]
+    margin = 1.05
+    for h in (0, 2):
+        q, k, _ = make_head(cfg, 0, 0, h)
+        Q, K = to_f64(q)[None, None], to_f64(k)[None, None]
+        b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        assert (b["stat_frame"][0, 0] > orc.BETA * margin).all(), h
+        g = orc.gap_bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+        qn = b["qnorm"][0, 0].reshape(cfg.F, cfg.T)
+        gap = g["gap"][0, 0].reshape(cfg.F, cfg.T)
+        for f in range(cfg.F):
+            # the band is where the norms are scaled: a contiguous run of hot_rows
+            med = np.median(qn[f])
+            hot = qn[f] > 1.6 * med
+            idx = np.flatnonzero(hot)
+            assert len(idx) > 0.9 * cfg.hot_rows and idx[-1] - idx[0] < cfg.hot_rows, (h, f)
+            assert gap[f, ~hot].max() < orc.GAP_LIMIT / 1.5, (h, f)
+            assert gap[f, hot].max() > orc.GAP_LIMIT * margin, (h, f)
+
+
+def test_cross_gap_bound_is_the_bound():
+    """Cross-attention: every row's slice is the whole reference set, so the
+    slice mean is mu and the gap bound equals the bound; it still brackets the
+    true gap (brute force)."""
+    rng = np.random.default_rng(9)
+    F, T, M, d = 3, 16, 24, 8
+    Q = rng.standard_normal((1, 1, F * T, d))
+    Kr = rng.standard_normal((1, 1, M, d)) + 2.0
+    b = orc.cross_bounds(Q, Kr, F, T, 0.5)
+    assert np.array_equal(b["gap"], b["bound"])
+    kc = Kr[0, 0] - Kr[0, 0].mean(axis=0)
+    true_gap = b["bound"][0, 0] - (0.5 * (Q[0, 0] @ kc.T)).max(axis=1)
+    assert np.all(true_gap <= b["gap"][0, 0] + 1e-12)
+
+
 # ---------------------------------------------------------------- routes
 
 def test_fixed_max_and_online_routes_equal_the_definition():
