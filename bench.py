@@ -249,7 +249,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="720p")
-    ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed", "auto_frame"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed", "auto_frame", "auto_rows"])
     ap.add_argument("--ab-launches", type=int, default=5,
                     help="timed online-only forward launches for the A/B figure")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

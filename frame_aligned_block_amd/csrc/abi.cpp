@@ -103,7 +103,7 @@ extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const voi
         return FSA_ERR_INVALID_ARG;
     }
     if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
-        mode != FSA_MODE_AUTO_FRAME) {
+        mode != FSA_MODE_AUTO_FRAME && mode != FSA_MODE_AUTO_ROWS) {
         set_error("fsa_forward: unknown mode %d", mode);
         return FSA_ERR_INVALID_ARG;
     }
@@ -218,7 +218,7 @@ fsa_status attend(const char* who, const void* Q, const void* K, const void* V, 
         return FSA_ERR_INVALID_ARG;
     }
     if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
-        mode != FSA_MODE_AUTO_FRAME) {
+        mode != FSA_MODE_AUTO_FRAME && mode != FSA_MODE_AUTO_ROWS) {
         set_error("%s: unknown mode %d", who, mode);
         return FSA_ERR_INVALID_ARG;
     }

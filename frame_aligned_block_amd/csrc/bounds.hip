@@ -239,6 +239,28 @@ __global__ __launch_bounds__(256) void bounds_finalize(
     }
 }
 
+// Pass 5, per (batch, head, query frame): the slice's mean key minus mu, from
+// the per-part column sums (parts never straddle a key frame). The gap bound
+// of a row, B_i - scale q_i.(kbar_S - mu), is at least how far the fixed max
+// lies above the row's largest logit, because a maximum is at least a mean.
+// Frames in run order, parts in order: a fixed summation order.
+__global__ __launch_bounds__(128) void bounds_slice_mean(
+    const float* __restrict__ colsum, const float* __restrict__ mu, float* __restrict__ dslice,
+    int F, int D, int KT, PartsArg kp, const FrameTable tab) {
+    const int f = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    if (t >= D) return;
+    const uint32_t run = tab.runs[f];
+    const int a0 = run & 0xff, l0 = (run >> 8) & 0xff;
+    const int a1 = (run >> 16) & 0xff, l1 = run >> 24;
+    const float* cs = colsum + size_t(bh) * kp.count * D + t;
+    float s = 0.f;
+    for (int g = a0; g < a0 + l0; ++g)
+        for (int q = 0; q < kp.per_frame; ++q) s += cs[size_t(g * kp.per_frame + q) * D];
+    for (int g = a1; g < a1 + l1; ++g)
+        for (int q = 0; q < kp.per_frame; ++q) s += cs[size_t(g * kp.per_frame + q) * D];
+    dslice[(size_t(bh) * F + f) * D + t] = s / float((l0 + l1) * KT) - mu[size_t(bh) * D + t];
+}
+
 template <typename E, int D>
 fsa_status run_bounds(const fsa_plan& p, const void* Qv, const void* Kv, void* wsv, float scale,
                       hipStream_t stream) {
@@ -289,6 +311,11 @@ fsa_status launch_bounds_finalize(const fsa_plan& p, char* ws, float scale, hipS
                        reinterpret_cast<float*>(ws + p.ws.statf),
                        reinterpret_cast<uint8_t*>(ws + p.ws.eligf), s.F, p.key_frames, qp, kp,
                        scale, p.table);
+    hipLaunchKernelGGL(bounds_slice_mean, dim3(s.F, s.B * s.H), dim3(128), 0, stream,
+                       reinterpret_cast<const float*>(ws + p.bounds.colsum),
+                       reinterpret_cast<const float*>(ws + p.ws.mu),
+                       reinterpret_cast<float*>(ws + p.ws.dslice), s.F, s.d, p.key_span, kp,
+                       p.table);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         set_error("bounds: launch failed: %s", hipGetErrorString(err));

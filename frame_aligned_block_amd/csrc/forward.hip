@@ -62,6 +62,7 @@ struct FwdArgs {
     const float* rslice;
     const uint8_t* elig;        // per (batch, head)
     const uint8_t* eligf;       // per (batch, head, frame)
+    const float* dslice;        // slice mean key minus mu, per (batch, head, frame)
     float c;                    // scale * log2(e)
     int32_t N, T, F, BH;
     int32_t NK;                 // key (and value) tokens per (batch, head)
@@ -102,11 +103,19 @@ __device__ __forceinline__ Slice slice_of(const FrameTable& t, int f, int KT) {
     return s;
 }
 
+// The route of a (batch*head, frame) pair from the flags of fsa_bounds. Under
+// AUTO_ROWS the kernels decide from the rows themselves (row_gap_ok).
 __device__ __forceinline__ bool use_fixed(const FwdArgs& p, int bh, int f) {
     if (p.mode == FSA_MODE_FIXED_ONLY) return true;
-    if (p.mode == FSA_MODE_ONLINE_ONLY) return false;
+    if (p.mode == FSA_MODE_ONLINE_ONLY || p.mode == FSA_MODE_AUTO_ROWS) return false;
     if (p.mode == FSA_MODE_AUTO_FRAME) return p.eligf[size_t(bh) * p.F + f] != 0;
     return p.elig[bh] != 0;
+}
+
+// Whether a gap bound, kept in units of 1/scale (||q_i|| R_S - q_i.dslice),
+// is within FSA_GAP_LIMIT once scaled: c = scale * log2(e).
+__device__ __forceinline__ bool row_gap_ok(float g, float c) {
+    return g * c <= FSA_GAP_LIMIT * kLog2e;
 }
 
 // Whether the (batch*head, frame) pairs of this launch take different routes
@@ -121,7 +130,8 @@ __device__ __forceinline__ bool routes_mixed(const FwdArgs& p) {
     if (p.mode == FSA_MODE_AUTO) {
         fl = p.elig;
         n = p.BH;
-    } else if (p.mode == FSA_MODE_AUTO_FRAME) {
+    } else if (p.mode == FSA_MODE_AUTO_FRAME || p.mode == FSA_MODE_AUTO_ROWS) {
+        // (AUTO_ROWS: the per-frame flags stand in for routes decided later)
         fl = p.eligf;
         n = p.BH * p.F;
     } else {
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 
     const size_t base = size_t(bh) * p.N * D, kbase = size_t(bh) * p.NK * D;
     const __bf16* Qh = static_cast<const __bf16*>(p.Q) + base;
-    const bool fixed = use_fixed(p, bh, f);              // uniform per workgroup
+    bool fixed = use_fixed(p, bh, f);                    // uniform per workgroup
     const __bf16* Kh = static_cast<const __bf16*>(p.K) + kbase;
     const __bf16* Vh = static_cast<const __bf16*>(p.V) + kbase;
     __bf16* Oh = static_cast<__bf16*>(p.O) + base;
@@ -751,7 +761,41 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     const int ngran = T >> 4;
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
-    if (__builtin_amdgcn_readfirstlane(nvalid) == 0) {
+    const bool idle = __builtin_amdgcn_readfirstlane(nvalid) == 0;
+    if (p.mode == FSA_MODE_AUTO_ROWS) {
+        // The workgroup takes the fixed max iff every one of its rows has its
+        // gap bound ||q_i|| R_S - q_i.dslice within the limit: each wave
+        // reduces its rows, the waves meet once in LDS (idle waves too).
+        __shared__ float wave_gap[fsa::kWaves];
+        float g = -INFINITY;
+        if (!idle) {
+            const float rsl = p.rslice[size_t(bh) * p.F + f];
+            const float* dsl = p.dslice + (size_t(bh) * p.F + f) * D;
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg) {
+                const int row = f * T + 16 * min(unit * G + gg, ngran - 1) + ln;
+                float dq = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < GG::KS; ++ks) {
+                    const bf16x8 q = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dq = fmaf(float(q[e]), dsl[32 * ks + 8 * lj + e], dq);
+                }
+                dq += __shfl_xor(dq, 16, 64);
+                dq += __shfl_xor(dq, 32, 64);
+                g = fmaxf(g, p.qnorm[size_t(bh) * p.N + row] * rsl - dq);
+            }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) g = fmaxf(g, __shfl_xor(g, o, 64));
+        }
+        if (lane == 0) wave_gap[wave] = g;
+        __syncthreads();
+        float wg = wave_gap[0];
+#pragma unroll
+        for (int w = 1; w < fsa::kWaves; ++w) wg = fmaxf(wg, wave_gap[w]);
+        fixed = row_gap_ok(wg, p.c);
+    }
+    if (idle) {
         copy_only<D>(smem, sl, Kh, Vh, fixed, uwave, lane);
         return;
     }
@@ -834,7 +878,7 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     const int T = p.T, f = i / T;
     const Slice sl = slice_of(p.tab, f, p.KT);
     const size_t base = size_t(bh) * p.N * D, kbase = size_t(bh) * p.NK * D;
-    const bool fixed = use_fixed(p, bh, f);
+    bool fixed = use_fixed(p, bh, f);
     const float* Qh = static_cast<const float*>(p.Q) + base;
     const float* Kh = static_cast<const float*>(p.K) + kbase;
     const float* Vh = static_cast<const float*>(p.V) + kbase;
@@ -850,7 +894,15 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     float qm = 0.f;                 // the fixed route scores K as given: shift by q.mu too
 #pragma unroll
     for (int e = 0; e < D; ++e) qm = fmaf(q[e], p.mu[size_t(bh) * D + e], qm);
-    const float shift = c * (p.qnorm[size_t(bh) * p.N + i] * p.rslice[size_t(bh) * p.F + f] + qm);
+    const float bnd = p.qnorm[size_t(bh) * p.N + i] * p.rslice[size_t(bh) * p.F + f];
+    if (p.mode == FSA_MODE_AUTO_ROWS) {        // this row's own gap bound
+        const float* dsl = p.dslice + (size_t(bh) * p.F + f) * D;
+        float dq = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) dq = fmaf(q[e], dsl[e], dq);
+        fixed = row_gap_ok(bnd - dq, c);
+    }
+    const float shift = c * (bnd + qm);
     float m = -INFINITY, rs = 0.f;
     for (int x = 0; x < sl.total; ++x) {
         const int j = sl.key(x);
@@ -903,6 +955,7 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
     a.rslice = reinterpret_cast<const float*>(ws + p.ws.rslice);
     a.elig = reinterpret_cast<const uint8_t*>(ws + p.ws.elig);
     a.eligf = reinterpret_cast<const uint8_t*>(ws + p.ws.eligf);
+    a.dslice = reinterpret_cast<const float*>(ws + p.ws.dslice);
     a.c = scale * kLog2e;
     a.N = s.F * s.T;
     a.NK = int32_t(p.key_tokens());

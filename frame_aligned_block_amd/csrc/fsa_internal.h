@@ -95,7 +95,9 @@ fsa_status launch_bounds(const fsa_plan& plan, const void* Q, const void* K, voi
                          float scale, hipStream_t stream);
 fsa_status launch_forward(const fsa_plan& plan, const void* Q, const void* K, const void* V,
                           void* O, const void* ws, float scale, int32_t mode, hipStream_t stream);
-// Per-frame and per-slice radii, statistics and flags from the per-part maxima.
+// Per-frame and per-slice radii, statistics and flags from the per-part maxima,
+// and each slice's mean-key offset from the per-part key column sums (the
+// workspace's colsum; both callers have written it).
 fsa_status launch_bounds_finalize(const fsa_plan& plan, char* ws, float scale, hipStream_t stream);
 // The producer (prep.hip).
 fsa_status launch_prep_fold(const void* W, const float* gamma, void* Wp, int32_t C,

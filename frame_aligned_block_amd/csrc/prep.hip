@@ -311,33 +311,42 @@ __global__ __launch_bounds__(256) void prep_mean(const float* __restrict__ ksum,
 }
 
 // Per part (at most 256 rows of one frame): the largest ||k_j - mu|| from the
-// keys and the largest ||q_i|| from the producer's row norms.
+// keys, the largest ||q_i|| from the producer's row norms, and the part's key
+// column sums (for the slices' mean keys; the producer's own sums are per
+// 256-token tile, which may straddle frames).
 template <int D>
 __global__ __launch_bounds__(256) void prep_radius(const __bf16* __restrict__ K,
                                                    const float* __restrict__ mu,
                                                    const float* __restrict__ qnorm,
                                                    float* __restrict__ partmax,
-                                                   float* __restrict__ partqmax, int N, int T,
+                                                   float* __restrict__ partqmax,
+                                                   float* __restrict__ colsum, int N, int T,
                                                    int rows_per_part, int ppf, int nparts) {
     constexpr int LPR = D / 8;
     constexpr int RPI = 256 / LPR;
     __shared__ float red[RPI], qred[256];
+    __shared__ float cred[RPI][D];
     const int part = blockIdx.x, bh = blockIdx.y;
     const int frame = part / ppf, sub = part % ppf;
     const int begin = frame * T + sub * rows_per_part;
     const int end = min(frame * T + T, begin + rows_per_part);
     const int lane = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
     const __bf16* Kh = K + size_t(bh) * N * D;
-    float m[8];
+    float m[8], acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = mu[size_t(bh) * D + lane * 8 + e];
+    for (int e = 0; e < 8; ++e) {
+        m[e] = mu[size_t(bh) * D + lane * 8 + e];
+        acc[e] = 0.f;
+    }
     float best = 0.f;
     for (int r = begin + r0; r < end; r += RPI) {
         const bf16x8 k = *reinterpret_cast<const bf16x8*>(Kh + size_t(r) * D + lane * 8);
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float c = float(k[e]) - m[e];
+            const float ke = float(k[e]);
+            acc[e] += ke;
+            const float c = ke - m[e];
             s = fmaf(c, c, s);
         }
 #pragma unroll
@@ -349,8 +358,15 @@ __global__ __launch_bounds__(256) void prep_radius(const __bf16* __restrict__ K,
         qb = fmaxf(qb, qnorm[size_t(bh) * N + r]);
     if (lane == 0) red[r0] = best;
     qred[threadIdx.x] = qb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cred[r0][lane * 8 + e] = acc[e];
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < D) {
+        float cs = 0.f;
+        for (int i = 0; i < RPI; ++i) cs += cred[i][threadIdx.x];
+        colsum[(size_t(bh) * nparts + part) * D + threadIdx.x] = cs;
+    }
+    if (threadIdx.x == D) {
         float b = 0.f, q = 0.f;
         for (int i = 0; i < RPI; ++i) b = fmaxf(b, red[i]);
         for (int i = 0; i < 256; ++i) q = fmaxf(q, qred[i]);
@@ -435,7 +451,8 @@ fsa_status launch_bounds_after_prep(const fsa_plan& p, const void* K, void* wsv,
                        reinterpret_cast<const float*>(ws + p.prep_ksum), mu, tiles, N);
     hipLaunchKernelGGL((prep_radius<128>), dim3(q.count(), BH), dim3(256), 0, stream,
                        static_cast<const __bf16*>(K), mu,
-                       reinterpret_cast<const float*>(ws + p.ws.qnorm), partmax, partqmax, N, s.T,
+                       reinterpret_cast<const float*>(ws + p.ws.qnorm), partmax, partqmax,
+                       reinterpret_cast<float*>(ws + p.bounds.colsum), N, s.T,
                        q.rows_per_part, q.per_frame, q.count());
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) {

@@ -35,10 +35,12 @@ FSA_MODE_AUTO = 0
 FSA_MODE_ONLINE_ONLY = 1
 FSA_MODE_FIXED_ONLY = 2
 FSA_MODE_AUTO_FRAME = 3
+FSA_MODE_AUTO_ROWS = 4
 MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MODE_FIXED_ONLY,
-         "auto_frame": FSA_MODE_AUTO_FRAME}
+         "auto_frame": FSA_MODE_AUTO_FRAME, "auto_rows": FSA_MODE_AUTO_ROWS}
 
 FSA_ELIG_BETA = 32.0
+FSA_GAP_LIMIT = 64.0
 FSA_MAX_FRAMES = 255
 
 # Every symbol include/fsa.h declares.
@@ -60,7 +62,7 @@ class fsa_shape(ctypes.Structure):
 
 class fsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("mu", "qnorm", "rframe", "rslice", "stat",
-                                         "elig", "statf", "eligf", "total")]
+                                         "elig", "statf", "eligf", "dslice", "total")]
 
 
 class FsaError(RuntimeError):
@@ -414,4 +416,5 @@ def workspace_views(plan: Plan, ws):
         "elig": view(lay["elig"], BH, torch.uint8, 1, (s.B, s.H)),
         "statf": view(lay["statf"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
         "eligf": view(lay["eligf"], BH * s.F, torch.uint8, 1, (s.B, s.H, s.F)),
+        "dslice": view(lay["dslice"], BH * s.F * s.d, torch.float32, 4, (s.B, s.H, s.F, s.d)),
     }

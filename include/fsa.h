@@ -84,13 +84,20 @@ typedef enum {
     FSA_MODE_ONLINE_ONLY = 1,   /* every head online (the A/B baseline)         */
     FSA_MODE_FIXED_ONLY = 2,    /* every head fixed max (tests: shows why the
                                    fallback exists; loose heads underflow)      */
-    FSA_MODE_AUTO_FRAME = 3     /* per (head, frame): fixed max where every row of
+    FSA_MODE_AUTO_FRAME = 3,    /* per (head, frame): fixed max where every row of
                                    the frame has its bound within FSA_ELIG_BETA,
                                    else online                                   */
+    FSA_MODE_AUTO_ROWS = 4      /* per block of query rows: fixed max where every
+                                   row of the block has its gap bound within
+                                   FSA_GAP_LIMIT, else online                    */
 } fsa_mode;
 
 /* Eligibility threshold on a head's largest row bound, in logit units. */
 #define FSA_ELIG_BETA 32.0f
+/* Limit on a row's gap bound (FSA_MODE_AUTO_ROWS), in logit units: twice
+   FSA_ELIG_BETA, the largest gap between the fixed max and a row's true max
+   that the per-head check allows (the logits of a row lie within +-B_i). */
+#define FSA_GAP_LIMIT 64.0f
 /* Largest frame count a plan accepts. */
 #define FSA_MAX_FRAMES 255
 
@@ -121,6 +128,8 @@ typedef struct {
     size_t statf;   /* per frame f: scale * max_{i in f} ||q_i|| rslice(f),
                        float [B][H][F]                                         */
     size_t eligf;   /* 1 if statf <= FSA_ELIG_BETA else 0, uint8 [B][H][F]     */
+    size_t dslice;  /* mean key of the slice S(f) minus mu, float [B][H][F][d]
+                       (a cross plan: the mean of all M keys minus their mu)   */
     size_t total;   /* bytes needed (== fsa_workspace_bytes)                   */
 } fsa_ws_layout;
 
@@ -188,8 +197,10 @@ fsa_status fsa_workspace_layout(const fsa_plan* plan, fsa_ws_layout* out);
  * fsa_bounds -- per (batch, head): key mean mu over all N keys (fp32, fixed
  * reduction order), per-frame max ||k_j - mu|| (fp32, from the keys as
  * given), per-slice max, row norms ||q_i||, the head statistic and its
- * eligibility flag ("Unchaining the Softmax" ¶2, ¶3). Q and K are only read
- * (no centred copy of K is written); results go to ws.
+ * eligibility flag ("Unchaining the Softmax" ¶2, ¶3), and per slice the
+ * offset of its mean key from mu (dslice) for the gap bound of
+ * FSA_MODE_AUTO_ROWS. Q and K are only read (no centred copy of K is
+ * written); results go to ws.
  * scale > 0 and finite. Deterministic: no atomics, fixed reduction trees.
  * Errors: FSA_ERR_INVALID_ARG (NULL plan/pointers, bad scale),
  * FSA_ERR_WORKSPACE (ws NULL or not 256-byte aligned), FSA_ERR_HIP.
@@ -199,14 +210,24 @@ fsa_status fsa_bounds(const fsa_plan* plan, const void* Q, const void* K, void* 
 
 /*
  * fsa_forward -- the attention itself, one launch. Reads Q, K, V and the
- * bound products in ws (mu, qnorm, rslice, elig) written by fsa_bounds for
- * the same plan, inputs and scale; writes O. Per (batch, head), mode picks the
+ * bound products in ws (mu, qnorm, rslice, elig, eligf, dslice) written by
+ * fsa_bounds (or fsa_bounds_after_prep) for the same plan, inputs and scale;
+ * writes O. Per (batch, head), mode picks the
  * route: AUTO takes the fixed max where elig = 1 and the online softmax
  * elsewhere (the per-head check of "Unchaining the Softmax" ¶3); AUTO_FRAME
  * decides per (batch, head, frame) from eligf instead, a finer check that is
  * as safe (every row of the frame has its bound within FSA_ELIG_BETA) and
  * keeps the frames of a loose head that never see its outlier keys on the
- * fixed route. Both routes score the keys as given. The fixed-max route shifts
+ * fixed route. AUTO_ROWS decides per block of query rows (a run of at most
+ * 256 consecutive rows of one frame, the rows one workgroup computes; one row
+ * in the fp32 kernel) from each row's gap bound
+ * G_i = B_i - scale q_i.(dslice(f)), B_i the row's Cauchy-Schwarz bound: a
+ * row's largest logit is at least the mean of its logits over its slice
+ * ("Unchaining the Softmax" ¶3: each row sees its own slice), so the fixed max
+ * exceeds it by at most G_i <= 2 B_i. A block takes the fixed max when every
+ * row has G_i <= FSA_GAP_LIMIT, which is the gap the per-head check allows,
+ * so the guarantee is the same row by row while looser heads keep most of
+ * their rows on the fixed route. Both routes score the keys as given. The fixed-max route shifts
  * row i by its Cauchy-Schwarz bound on the centred scores plus scale q_i.mu:
  * centring by mu moves every score of the row by that same amount, so the
  * softmax is unchanged and the shift bounds the raw scores ("Unchaining the

@@ -116,7 +116,7 @@ def test_attention_validates_before_launch():
         (dict(d=32), fsa.FSA_ERR_UNSUPPORTED),
         (dict(ref_frame=9), fsa.FSA_ERR_INVALID_ARG),
         (dict(scale=float("inf")), fsa.FSA_ERR_INVALID_ARG),
-        (dict(mode=4), fsa.FSA_ERR_INVALID_ARG),
+        (dict(mode=5), fsa.FSA_ERR_INVALID_ARG),
         (dict(mode=-1), fsa.FSA_ERR_INVALID_ARG),
         (dict(O=FAKE * 64), fsa.FSA_ERR_INVALID_ARG),        # O == K
         (dict(V=None), fsa.FSA_ERR_INVALID_ARG),

@@ -104,6 +104,10 @@ def check_stats_and_bounds(run, heads):
             assert int(v["elig"][b, h]) == int(want["elig"][0, 0]), (b, h)
             assert np.array_equal(v["eligf"][b, h].cpu().numpy().astype(bool),
                                   want["elig_frame"][0, 0])
+            gb = orc.gap_bounds(q[None, None], k[None, None], cfg.F, cfg.T, cfg.window,
+                                cfg.ref_frame, cfg.scale)
+            ds = v["dslice"][b, h].double().cpu().numpy()
+            assert np.max(np.abs(ds - gb["dslice"][0, 0])) < 1e-4, (b, h)
 
 
 def test_prep_small_full():
@@ -137,6 +141,8 @@ def test_prep_feeds_the_attention():
         float((a["qnorm"] - c["qnorm"]).abs().max()) < 1e-5
     for k in ("mu", "rframe", "rslice", "stat", "statf"):
         assert torch.allclose(a[k], c[k], rtol=1e-5, atol=1e-6), k
+    # slice mean minus mu: the two routes take mu from different sum orders
+    assert float((a["dslice"] - c["dslice"]).abs().max()) < 1e-5
     for k in ("elig", "eligf"):
         assert torch.equal(a[k], c[k]), k
 

@@ -56,7 +56,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
     B, H, N, d, F = 1, 24, 13 * 3600, 128, 13
     sizes = {"mu": B * H * d * 4, "qnorm": B * H * N * 4,
              "rframe": B * H * F * 4, "rslice": B * H * F * 4, "stat": B * H * 4, "elig": B * H,
-             "statf": B * H * F * 4, "eligf": B * H * F}
+             "statf": B * H * F * 4, "eligf": B * H * F, "dslice": B * H * F * d * 4}
     spans = sorted((lay[k], lay[k] + n) for k, n in sizes.items())
     for (a0, e0), (a1, _) in zip(spans, spans[1:]):
         assert e0 <= a1
@@ -111,7 +111,8 @@ def test_cross_workspace_layout():
     # radii as for self-attention
     assert lay["rslice"] - lay["rframe"] == 256
     sizes = {"mu": H * 128 * 4, "qnorm": H * F * T * 4, "rframe": H * 4, "rslice": H * F * 4,
-             "stat": H * 4, "elig": H, "statf": H * F * 4, "eligf": H * F}
+             "stat": H * 4, "elig": H, "statf": H * F * 4, "eligf": H * F,
+             "dslice": H * F * 128 * 4}
     spans = sorted((lay[k], lay[k] + n) for k, n in sizes.items())
     for (a0, e0), (a1, _) in zip(spans, spans[1:]):
         assert e0 <= a1
