@@ -77,6 +77,7 @@ struct fsa_plan {
     fsa::ForwardGeometry forward;
     fsa_ws_layout ws;
     size_t prep_ksum = 0;            // private ws: producer's key column sums, [BH][tiles][d]
+    size_t prep_rscale = 0;          // private ws: producer's RMSNorm row scales, [B][N]
 };
 
 namespace fsa {

@@ -228,6 +228,7 @@ fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const c
         if (!cross) {        // the producer's per-tile key column sums
             const size_t tiles = size_t((N + kPrepTile - 1) / kPrepTile);
             p->prep_ksum = off; off = align_up(off + BH * tiles * s.d * 4);
+            p->prep_rscale = off; off = align_up(off + size_t(s.B) * N * 4);
         }
         w.total = off;
     } catch (const std::bad_alloc&) {

@@ -19,14 +19,23 @@
 // and the row scale rsqrt(mean(x^2) + eps) is applied in the epilogue, which is
 // exact: (x * s * gamma) W^T = s * (x W'^T).
 //
-// gfx950 design: one workgroup of 4 waves (two workgroups per CU, so two
-// waves per SIMD) computes a 256-token x 128-channel tile (one head of q, k or
-// v) as the transposed product Y^T = W' X^T on v_mfma_f32_16x16x32_bf16; each
-// wave owns 64 tokens of the head, so a lane ends with 4 tokens and 4
-// consecutive channels of each 16-channel block: rotation pairs are in-lane,
-// and the row norm reduces like the attention's row sums. W' and X tiles
-// stream through a two-stage LDS ring of 32-channel chunks (2 x 24 KB) by
-// direct-to-LDS copies, as the attention's K and V do.
+// gfx950 design: the projection is a plain GEMM of 46,800 x 9,216 x 3,072 at
+// the 720p shape, so its tiles are sized for the matrix cores rather than for
+// latency hiding by occupancy: one workgroup of 4 waves per CU (one wave per
+// SIMD, 512 registers per lane) computes a 256-token x 256-channel tile (two
+// heads of q, k or v) as the transposed product Y^T = W' X^T on
+// v_mfma_f32_16x16x32_bf16. Each wave owns 128 tokens of one head: its 64
+// accumulators (256 registers) sit in the accumulation registers, and a lane
+// ends with 4 consecutive channels of each 16-channel block of each of its
+// tokens, so rotation pairs are in-lane and the row norm reduces like the
+// attention's row sums. W' and X stream through a four-stage LDS ring of
+// 32-channel chunks (4 x 32 KB) by direct-to-LDS copies issued three chunks
+// ahead. A wave's copies are spread among its products: a wave stalls while
+// the CU's address unit works through its copies, and with one wave per SIMD
+// nothing else feeds the matrix unit meanwhile. While a chunk's 64 products
+// run, the wave already reads the next chunk's operands. The RMSNorm row
+// scales come from a short pre-pass over X (prep_rowscale), so the GEMM loop
+// does no vector arithmetic at all.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,22 +49,24 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;                 // two workgroups (two waves per SIMD) per CU
-constexpr int kTG = 64;                   // tokens per wave (4 granules of 16)
-constexpr int kTok = fsa::kPrepTile;      // tokens per tile: 4 wave rows of 64
-static_assert(kTok == 4 * kTG, "4 rows of waves");
+constexpr int kWaves = 4;                 // one workgroup (one wave per SIMD) per CU
+constexpr int kTG = 128;                  // tokens per wave (8 granules of 16)
+constexpr int kTok = fsa::kPrepTile;      // tokens per tile
+constexpr int kWRows = kTok / kTG;        // wave rows of a tile
 constexpr int kCh = 128;                  // output channels per wave: one head of width 128
-constexpr int kCols = kWaves / 4;         // heads per workgroup (one wave column of 4)
+constexpr int kCols = kWaves / kWRows;    // heads per workgroup: wave columns
+static_assert(kCols * kWRows == kWaves, "waves tile the workgroup");
 constexpr int kRows = kCols * kCh;        // W' rows of a tile
 constexpr int kKC = 32;                   // input channels per LDS chunk (one k-step)
-constexpr int kSubs = kKC / 32;           // 32-column sub-tiles per chunk
-constexpr int kWSub = kRows * 64;         // a [256 rows][32 columns] sub-tile of W', bytes
+constexpr int kWSub = kRows * 64;         // a [256 rows][32 columns] chunk of W', bytes
 constexpr int kXSub = kTok * 64;          // the same for X
-constexpr int kWTile = kSubs * kWSub;
-constexpr int kStage = kWTile + kSubs * kXSub;
-// Direct-to-LDS copies address LDS through the low 16 bits of M0: the ring
-// must sit in the first 64 KB.
-static_assert(2 * kStage <= 65536, "copy ring within the first 64 KB of LDS");
+constexpr int kStage = kWSub + kXSub;
+constexpr int kStages = 4;                // LDS ring depth: copies run kStages-1 chunks ahead
+constexpr int kPerCU = 1;                 // workgroups per CU
+static_assert(kPerCU * (kStages * kStage + kWaves * 128 * 4) <= 160 * 1024, "rings within the CU's 160 KB of LDS");
+constexpr int kCopyWaves = kWaves;        // waves that issue the direct-to-LDS copies
+constexpr int kCopiesPerChunk = (kRows + kTok) / 16 / kCopyWaves;   // copies per copy wave
+static_assert(kCopiesPerChunk <= kCh / 16, "one copy after each run of products");
 constexpr int kMaxPairs = 64;             // channel pairs of a head (d <= 128)
 
 struct PrepArgs {
@@ -66,6 +77,7 @@ struct PrepArgs {
     void* V;
     float* qnorm;         // [B][H][N]: ||q|| of the bf16 outputs
     float* ksum;          // [B][H][tiles][d]: per-tile column sums of the bf16 keys
+    const float* rscale;  // [B][N]: 1 / sqrt(mean(x^2) + eps)
     int32_t B, H, N, C, T, Wg, tiles, pairs;
     int32_t nwg;
     float eps;
@@ -85,50 +97,88 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
                  :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Copies of input-channel chunk kc: the W' tile (the head's 128 output
-// channels) and the X tile (256 tokens, rows past the last repeat it; never
-// stored), as sub-tiles of 32 columns in blocks of 16 rows; wave w copies the
-// blocks j = 4i + w. The 16-byte segment is swizzled by (row >> 1) & 3.
-// (Workgroups stay at 4 waves: in 8-wave workgroups, direct-to-LDS copies to
-// some destinations were measured not to land.)
-constexpr int kCopyWaves = 4;
+// Copy i (0 <= i < kCopiesPerChunk) of copy wave `wave`'s share of input
+// channel chunk kc. The chunk is kRows/16 blocks of W' (the workgroup's
+// output channels; rows past the last head repeat it, never stored), then
+// kTok/16 blocks of X (rows past the last token repeat it, never stored),
+// each 16 rows x 64 bytes; copy wave w takes blocks j = kCopyWaves * i + w.
+// The 16-byte segment is swizzled by (row >> 1) & 3.
+__device__ __forceinline__ void issue_copy(unsigned stage, const unsigned char* Wrows, int nwrows,
+                                           const unsigned char* Xrows, int ntok, int C, int kc,
+                                           int wave, int lane, int i) {
+    const int seg = lane & 3, rr = lane >> 2;
+    const unsigned col = unsigned(kc * kKC) * 2 + 16 * (seg ^ ((lane >> 3) & 3));
+    const int j = kCopyWaves * i + wave;
+    if (j < kRows / 16) {
+        const int wrow = min(16 * j + rr, nwrows - 1);
+        lds_copy16(stage + j * 1024, Wrows, unsigned(wrow) * unsigned(C) * 2 + col);
+    } else {
+        const int rb = j - kRows / 16;
+        const int xrow = min(16 * rb + rr, ntok - 1);
+        lds_copy16(stage + kWSub + rb * 1024, Xrows, unsigned(xrow) * unsigned(C) * 2 + col);
+    }
+}
 
+// All of a copy wave's copies of chunk kc; other waves issue none.
 __device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows, int nwrows,
                                             const unsigned char* Xrows, int ntok, int C, int kc,
                                             int wave, int lane) {
     if (wave >= kCopyWaves) return;
-    const int seg = lane & 3, rr = lane >> 2;
-    const unsigned sw = 16 * (seg ^ ((lane >> 3) & 3));
-    constexpr int WB = kSubs * kRows / 16, XB = kSubs * kTok / 16;   // 16-row blocks
 #pragma unroll
-    for (int i = 0; i < WB / kCopyWaves; ++i) {
-        const int j = kCopyWaves * i + wave;
-        const int t = j / (kRows / 16), rb = j % (kRows / 16);
-        const unsigned col = unsigned(kc * kKC + 32 * t) * 2 + sw;
-        const int wrow = min(16 * rb + rr, nwrows - 1);
-        lds_copy16(stage + t * kWSub + rb * 1024, Wrows, unsigned(wrow) * unsigned(C) * 2 + col);
+    for (int i = 0; i < kCopiesPerChunk; ++i)
+        issue_copy(stage, Wrows, nwrows, Xrows, ntok, C, kc, wave, lane, i);
+}
+
+// This wave's operands of one chunk: its 8 token granules of X and its head's
+// 8 channel blocks of W', each one 16-byte read per lane.
+template <int G, int NB>
+__device__ __forceinline__ void load_operands(const unsigned char* S, int wr, int wc, int ka,
+                                              bf16x8 (&xb)[G], bf16x8 (&wa)[NB]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        xb[g] = *reinterpret_cast<const bf16x8*>(S + kWSub + (kTG * wr + 16 * g) * 64 + ka);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+        wa[cb] = *reinterpret_cast<const bf16x8*>(S + (kCh * wc + 16 * cb) * 64 + ka);
+}
+
+template <int G, int NB, typename Between>
+__device__ __forceinline__ void products(const bf16x8 (&xb)[G], const bf16x8 (&wa)[NB],
+                                         f32x4 (&acc)[G][NB], Between between) {
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cb], xb[g], acc[g][cb], 0, 0, 0);
+        between(cb);            // after each run of G products
+        __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < XB / kCopyWaves; ++i) {
-        const int j = kCopyWaves * i + wave;
-        const int t = j / (kTok / 16), rb = j % (kTok / 16);
-        const unsigned col = unsigned(kc * kKC + 32 * t) * 2 + sw;
-        const int xrow = min(16 * rb + rr, ntok - 1);
-        lds_copy16(stage + kWTile + t * kXSub + rb * 1024, Xrows,
-                   unsigned(xrow) * unsigned(C) * 2 + col);
+}
+
+// Wait until at most `later` chunks' copies of this wave are still in flight
+// (loads complete in issue order), i.e. until the chunk issued just before
+// them has landed. 0 <= later < kStages.
+#define PREP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+__device__ __forceinline__ void wait_chunk(int later) {
+    static_assert(kStages <= 4 && kCopiesPerChunk * 3 <= 63, "vmcnt field");
+    switch (later) {
+        case 3: PREP_VMCNT(kCopiesPerChunk * 3); break;
+        case 2: PREP_VMCNT(kCopiesPerChunk * 2); break;
+        case 1: PREP_VMCNT(kCopiesPerChunk); break;
+        default: PREP_VMCNT(0); break;
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
+__global__ __launch_bounds__(kWaves * 64, kPerCU) void prep_qkv(const PrepArgs p) {
     static_assert(D == kCh, "one 128-channel head per wave column");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStage];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
     __shared__ float red[kWaves][D];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
-    const int wr = uwave & 3, wc = uwave >> 2;             // wave row (tokens), column (head)
+    const int wr = uwave % kWRows, wc = uwave / kWRows;    // wave row (tokens), column (head)
 
     // Workgroups walk (8 token tiles) x (all head pairs) groups, so that the
     // ones an XCD runs at once share X chunks and W' chunks.
@@ -153,54 +203,61 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
     const int nchunks = p.C / kKC;
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
 
-    constexpr int G = kTG / 16;
-    f32x4 acc[G][D / 16];
+    constexpr int G = kTG / 16, NB = D / 16;
+    f32x4 acc[G][NB];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) acc[g][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss[G];                             // sum of x^2 of this lane's tokens
-#pragma unroll
-    for (int g = 0; g < G; ++g) ss[g] = 0.f;
+        for (int cb = 0; cb < NB; ++cb) acc[g][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ka = ln * 64 + 16 * (lj ^ ((ln >> 1) & 3));    // this lane's 16 bytes of a 16-row block
-    issue_chunk(smem_lds, Wrows, nwrows, Xrows, ntok, p.C, 0, uwave, lane);
-    PREP_WAIT_VMCNT0();
+    // Chunk c lives in stage c % kStages. The ring starts full.
+    for (int c = 0; c < kStages && c < nchunks; ++c)
+        issue_chunk(smem_lds + c * kStage, Wrows, nwrows, Xrows, ntok, p.C, c, uwave, lane);
+    wait_chunk(min(kStages, nchunks) - 1);               // chunk 0 has landed
     __builtin_amdgcn_s_barrier();
-    if (nchunks > 1) issue_chunk(smem_lds + kStage, Wrows, nwrows, Xrows, ntok, p.C, 1, uwave, lane);
-    int st = 0;
-    for (int kc = 0; kc < nchunks; ++kc) {
-        const unsigned char* S0 = smem + st * kStage;
-#pragma unroll
-        for (int ks = 0; ks < kSubs; ++ks) {
-            bf16x8 xb[G], wa[D / 16];
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                xb[g] = *reinterpret_cast<const bf16x8*>(S0 + kWTile + ks * kXSub +
-                                                         (kTG * wr + 16 * g) * 64 + ka);
-#pragma unroll
-            for (int cb = 0; cb < D / 16; ++cb)
-                wa[cb] = *reinterpret_cast<const bf16x8*>(S0 + ks * kWSub +
-                                                          (kCh * wc + 16 * cb) * 64 + ka);
-#pragma unroll
-            for (int cb = 0; cb < D / 16; ++cb)
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[cb], xb[g], acc[g][cb], 0, 0, 0);
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss[g] = fmaf(float(xb[g][e]), float(xb[g][e]), ss[g]);
-        }
-        if (kc + 1 < nchunks) {
-            PREP_WAIT_VMCNT0();                          // chunk kc+1 has landed
+    bf16x8 xb[2][G], wa[2][NB];
+    load_operands<G, NB>(smem, wr, wc, ka, xb[0], wa[0]);
+    // One chunk: once chunk k+1 has landed and every wave holds its chunk-k
+    // operands, chunk k's stage takes chunk k + kStages; then the wave reads
+    // chunk k+1's operands while chunk k's products run. Two chunks per trip,
+    // so each operand set keeps its registers. In the steady state two later
+    // chunks' copies of this wave may still be in flight; near the end the
+    // wave waits for all of them.
+    auto step = [&](int k, int u, bool steady) {
+        if (steady || k + 1 < nchunks) {
+            if (steady) PREP_VMCNT(kCopiesPerChunk * (kStages - 2));
+            else PREP_VMCNT(0);
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4));   // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
-            if (kc + 2 < nchunks)
-                issue_chunk(smem_lds + st * kStage, Wrows, nwrows, Xrows, ntok, p.C, kc + 2, uwave,
-                            lane);
-            st ^= 1;
+            load_operands<G, NB>(smem + ((k + 1) % kStages) * kStage, wr, wc, ka, xb[u ^ 1],
+                                 wa[u ^ 1]);
         }
+        // Keep the products after the reads they overlap (the compiler would
+        // otherwise hoist them above the barrier and leave the reads exposed),
+        // and spread this wave's copies of chunk k + kStages among them: a
+        // wave stalls while the CU's address unit works through its copies,
+        // and no other wave on the SIMD covers that here.
+        __builtin_amdgcn_sched_barrier(0);
+        const bool copies = steady || (k + 1 < nchunks && k + kStages < nchunks);
+        const unsigned stage = smem_lds + (k % kStages) * kStage;
+        products<G, NB>(xb[u], wa[u], acc, [&](int cb) {
+            if (copies && uwave < kCopyWaves && cb < kCopiesPerChunk)
+                issue_copy(stage, Wrows, nwrows, Xrows, ntok, p.C, k + kStages, uwave, lane, cb);
+        });
+    };
+    // Steady trips have no branch inside: chunk k+1 exists, chunks k+2 and
+    // k+3 were issued after it, and chunk k + kStages exists (k + 1 + kStages
+    // < nchunks for both steps of the trip).
+    const int steady_end = max(0, (nchunks - kStages) & ~1);
+    int kc = 0;
+    for (; kc < steady_end; kc += 2) {
+        step(kc, 0, true);
+        step(kc + 1, 1, true);
+    }
+    for (; kc < nchunks; kc += 2) {
+        step(kc, 0, false);
+        if (kc + 1 < nchunks) step(kc + 1, 1, false);
     }
     PREP_WAIT_VMCNT0();
 
@@ -208,24 +265,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
     const bool rotate = part < 2;
     __bf16* out = static_cast<__bf16*>(part == 0 ? p.Q : part == 1 ? p.K : p.V) +
                   (size_t(b) * p.H + h) * p.N * D;
-    float csum[D / 16][4];                   // key column sums over this lane's tokens
+    float csum[NB][4];                       // key column sums over this lane's tokens
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb)
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) csum[cb][e] = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        float s2 = ss[g] + __shfl_xor(ss[g], 16, 64);
-        s2 += __shfl_xor(s2, 32, 64);
-        const float rs = 1.0f / sqrtf(s2 / float(p.C) + p.eps);
         const int tl = kTG * wr + 16 * g + ln;           // token within the tile
         const bool live = col_live && tl < ntok;
         const int n = tok0 + min(tl, ntok - 1);
+        const float rs = p.rscale[size_t(b) * p.N + n];
         const int f = n / p.T, pin = n % p.T;
         const float pos[3] = {float(f), float(pin / p.Wg), float(pin % p.Wg)};
         float qq = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) {
+        for (int cb = 0; cb < NB; ++cb) {
             float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) y[e] = acc[g][cb][e] * rs;
@@ -260,10 +315,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
             if (live && lj == 0) p.qnorm[(size_t(b) * p.H + h) * p.N + n] = sqrtf(qq);
         }
     }
-    // key column sums: over the 16 tokens of each lane group, then the 4 wave
+    // key column sums: over the 16 tokens of each lane group, then the 2 wave
     // rows of the column, in order (every wave passes the same barrier)
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb)
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = csum[cb][e];
@@ -276,11 +331,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prep_qkv(const PrepArgs p) {
     __syncthreads();
     if (part == 1 && col_live && wr == 0) {
         for (int c = lane; c < D; c += 64) {
-            const float s = ((red[4 * wc][c] + red[4 * wc + 1][c]) + red[4 * wc + 2][c]) +
-                            red[4 * wc + 3][c];
+            float s = red[kWRows * wc][c];
+#pragma unroll
+            for (int r = 1; r < kWRows; ++r) s += red[kWRows * wc + r][c];
             p.ksum[((size_t(b) * p.H + h) * p.tiles + tile) * D + c] = s;
         }
     }
+}
+
+// RMSNorm row scale of every token: 1 / sqrt(mean_c x_c^2 + eps), fp32 from
+// the bf16 tokens; 16 lanes per token, 16 tokens per workgroup.
+__global__ __launch_bounds__(256) void prep_rowscale(const __bf16* __restrict__ X,
+                                                     float* __restrict__ rscale, int64_t rows,
+                                                     int C, float eps) {
+    const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    if (row >= rows) return;                 // whole 16-lane groups: the shuffles stay in-group
+    const __bf16* x = X + row * C;
+    float s = 0.f;
+    for (int c = 8 * l; c < C; c += 128) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(float(v[e]), float(v[e]), s);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
+    if (l == 0) rscale[row] = 1.0f / sqrtf(s / float(C) + eps);
 }
 
 // W' = W * gamma (per input channel), rounded to bf16.
@@ -405,6 +481,7 @@ fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void*
     a.V = V;
     a.qnorm = reinterpret_cast<float*>(ws + p.ws.qnorm);
     a.ksum = reinterpret_cast<float*>(ws + p.prep_ksum);
+    a.rscale = reinterpret_cast<const float*>(ws + p.prep_rscale);
     a.B = s.B;
     a.H = s.H;
     a.N = s.F * s.T;
@@ -428,6 +505,10 @@ fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void*
         return FSA_ERR_UNSUPPORTED;
     }
     a.nwg = int32_t(nwg);
+    const int64_t rows = int64_t(s.B) * a.N;
+    hipLaunchKernelGGL(prep_rowscale, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(X), reinterpret_cast<float*>(ws + p.prep_rscale),
+                       rows, a.C, a.eps);
     hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(kWaves * 64), 0, stream, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
