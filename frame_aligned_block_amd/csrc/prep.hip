@@ -20,22 +20,20 @@
 // exact: (x * s * gamma) W^T = s * (x W'^T).
 //
 // gfx950 design: the projection is a plain GEMM of 46,800 x 9,216 x 3,072 at
-// the 720p shape, so its tiles are sized for the matrix cores rather than for
-// latency hiding by occupancy: one workgroup of 4 waves per CU (one wave per
-// SIMD, 512 registers per lane) computes a 256-token x 256-channel tile (two
-// heads of q, k or v) as the transposed product Y^T = W' X^T on
-// v_mfma_f32_16x16x32_bf16. Each wave owns 128 tokens of one head: its 64
-// accumulators (256 registers) sit in the accumulation registers, and a lane
-// ends with 4 consecutive channels of each 16-channel block of each of its
-// tokens, so rotation pairs are in-lane and the row norm reduces like the
-// attention's row sums. W' and X stream through a four-stage LDS ring of
-// 32-channel chunks (4 x 32 KB) by direct-to-LDS copies issued three chunks
-// ahead. A wave's copies are spread among its products: a wave stalls while
-// the CU's address unit works through its copies, and with one wave per SIMD
-// nothing else feeds the matrix unit meanwhile. While a chunk's 64 products
-// run, the wave already reads the next chunk's operands. The RMSNorm row
-// scales come from a short pre-pass over X (prep_rowscale), so the GEMM loop
-// does no vector arithmetic at all.
+// the 720p shape. One workgroup of 8 waves per CU (two waves per SIMD)
+// computes a 256-token x 256-channel tile (two heads of q, k or v) as the
+// transposed product Y^T = W' X^T on v_mfma_f32_16x16x32_bf16. Each wave owns
+// 64 tokens of one head (32 accumulators, 128 registers); a lane ends with 4
+// consecutive channels of each 16-channel block of each of its tokens, so
+// rotation pairs are in-lane and the row norm reduces like the attention's
+// row sums. W' and X stream through a four-stage LDS ring of 32-channel
+// chunks (4 x 32 KB) by direct-to-LDS copies issued three chunks ahead, each
+// wave's share spread among its products: issuing a copy stalls the wave
+// while the CU's address unit works through the queue, and the other wave on
+// the SIMD keeps the matrix unit busy meanwhile. While a chunk's products run,
+// the wave already reads the next chunk's operands. The RMSNorm row scales
+// come from a short pre-pass over X (prep_rowscale), so the GEMM loop does no
+// vector arithmetic at all.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -49,13 +47,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;                 // one workgroup (one wave per SIMD) per CU
-constexpr int kTG = 128;                  // tokens per wave (8 granules of 16)
+constexpr int kPrepWaves = 8;             // waves of a workgroup: two per SIMD, one workgroup per CU
+constexpr int kTG = 64;                   // tokens per wave (4 granules of 16)
 constexpr int kTok = fsa::kPrepTile;      // tokens per tile
 constexpr int kWRows = kTok / kTG;        // wave rows of a tile
 constexpr int kCh = 128;                  // output channels per wave: one head of width 128
-constexpr int kCols = kWaves / kWRows;    // heads per workgroup: wave columns
-static_assert(kCols * kWRows == kWaves, "waves tile the workgroup");
+constexpr int kCols = kPrepWaves / kWRows;    // heads per workgroup: wave columns
+static_assert(kCols * kWRows == kPrepWaves, "waves tile the workgroup");
 constexpr int kRows = kCols * kCh;        // W' rows of a tile
 constexpr int kKC = 32;                   // input channels per LDS chunk (one k-step)
 constexpr int kWSub = kRows * 64;         // a [256 rows][32 columns] chunk of W', bytes
@@ -63,8 +61,8 @@ constexpr int kXSub = kTok * 64;          // the same for X
 constexpr int kStage = kWSub + kXSub;
 constexpr int kStages = 4;                // LDS ring depth: copies run kStages-1 chunks ahead
 constexpr int kPerCU = 1;                 // workgroups per CU
-static_assert(kPerCU * (kStages * kStage + kWaves * 128 * 4) <= 160 * 1024, "rings within the CU's 160 KB of LDS");
-constexpr int kCopyWaves = kWaves;        // waves that issue the direct-to-LDS copies
+static_assert(kPerCU * (kStages * kStage + kPrepWaves * 128 * 4) <= 160 * 1024, "rings within the CU's 160 KB of LDS");
+constexpr int kCopyWaves = kPrepWaves;    // waves that issue the direct-to-LDS copies
 constexpr int kCopiesPerChunk = (kRows + kTok) / 16 / kCopyWaves;   // copies per copy wave
 static_assert(kCopiesPerChunk <= kCh / 16, "one copy after each run of products");
 constexpr int kMaxPairs = 64;             // channel pairs of a head (d <= 128)
@@ -170,10 +168,10 @@ __device__ __forceinline__ void wait_chunk(int later) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, kPerCU) void prep_qkv(const PrepArgs p) {
+__global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepArgs p) {
     static_assert(D == kCh, "one 128-channel head per wave column");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * kStage];
-    __shared__ float red[kWaves][D];
+    __shared__ float red[kPrepWaves][D];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
@@ -509,7 +507,7 @@ fsa_status launch_prep(const fsa_plan& p, int32_t Wg, const void* X, const void*
     hipLaunchKernelGGL(prep_rowscale, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, stream,
                        static_cast<const __bf16*>(X), reinterpret_cast<float*>(ws + p.prep_rscale),
                        rows, a.C, a.eps);
-    hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL((prep_qkv<128>), dim3(a.nwg), dim3(kPrepWaves * 64), 0, stream, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {
         set_error("fsa_prep: launch failed: %s", hipGetErrorString(err));
