@@ -128,10 +128,14 @@ def test_prep_feeds_the_attention():
     O = torch.empty_like(run.Q)
     fsa.fsa_forward(run.plan, run.Q, run.K, run.V, O, run.ws, cfg.scale, "auto")
     torch.cuda.synchronize()
+    O_rows = torch.empty_like(run.Q)          # the row-block route reads the slice offsets
+    fsa.fsa_forward(run.plan, run.Q, run.K, run.V, O_rows, run.ws, cfg.scale, "auto_rows")
+    torch.cuda.synchronize()
     for h in range(cfg.H):
         rows = sample_rows(cfg, 200, seed=h)
         want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
         assert_close(cfg, O[0, h, rows], want, f"prep->attention head {h}")
+        assert_close(cfg, O_rows[0, h, rows], want, f"prep->attention auto_rows head {h}")
     ws2 = torch.zeros_like(run.ws)
     fsa.fsa_bounds(run.plan, run.Q, run.K, ws2, cfg.scale)
     torch.cuda.synchronize()

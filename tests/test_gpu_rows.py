@@ -187,3 +187,39 @@ def test_auto_rows_cross():
         rows = sample_rows(cfg, 150, seed=h)
         want = oracle_cross_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
         assert_close(cfg, O_rows[0, h, rows], want, f"auto_rows cross head {h}")
+
+
+@pytest.mark.parametrize("name,kw,block", [
+    ("d64", dict(d=64), 256),                 # 4 waves x 64 rows at d = 64
+    ("batch-2", dict(B=2), 128),
+    ("short-frames", dict(T=144, hot_rows=16), 128),   # a 128-row block and a 16-row one
+])
+def test_auto_rows_edge_shapes(name, kw, block):
+    """AUTO_ROWS on other shapes: the d = 64 kernel's 256-row blocks, two
+    batches, frames shorter than one block. Blocks clear of the limit match
+    FIXED_ONLY or ONLINE_ONLY bit for bit; all rows meet the bar."""
+    cfg = CONFIGS["loose-rows-small"].with_(**kw)
+    say("auto_rows edge", name)
+    run = Run(cfg).bounds()
+    O_rows = run.forward("auto_rows")
+    O_fix = run.forward("fixed")
+    O_onl = run.forward("online")
+    n_fix = n_onl = 0
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            q = to_f64(run.Q[b, h])[None, None]
+            k = to_f64(run.K[b, h])[None, None]
+            gap = orc.gap_bounds(q, k, cfg.F, cfg.T, cfg.window, cfg.ref_frame,
+                                 cfg.scale)["gap"][0, 0]
+            for f, a, e in row_blocks(cfg.T, cfg.F, block):
+                g = gap[a:e].max()
+                if g < orc.GAP_LIMIT * (1 - CLEAR):
+                    assert torch.equal(O_rows[b, h, a:e], O_fix[b, h, a:e]), (b, h, f, a)
+                    n_fix += 1
+                elif g > orc.GAP_LIMIT * (1 + CLEAR):
+                    assert torch.equal(O_rows[b, h, a:e], O_onl[b, h, a:e]), (b, h, f, a)
+                    n_onl += 1
+            rows = sample_rows(cfg, 100, seed=h)
+            want = oracle_rows(cfg, run.Q, run.K, run.V, b, h, rows)
+            assert_close(cfg, O_rows[b, h, rows], want, f"auto_rows {name} b{b} h{h}")
+    assert n_fix > 0 and n_onl > 0, (n_fix, n_onl)
