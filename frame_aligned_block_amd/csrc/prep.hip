@@ -62,8 +62,7 @@ constexpr int kStage = kWSub + kXSub;
 constexpr int kStages = 4;                // LDS ring depth: copies run kStages-1 chunks ahead
 constexpr int kPerCU = 1;                 // workgroups per CU
 static_assert(kPerCU * (kStages * kStage + kPrepWaves * 128 * 4) <= 160 * 1024, "rings within the CU's 160 KB of LDS");
-constexpr int kCopyWaves = kPrepWaves;    // waves that issue the direct-to-LDS copies
-constexpr int kCopiesPerChunk = (kRows + kTok) / 16 / kCopyWaves;   // copies per copy wave
+constexpr int kCopiesPerChunk = (kRows + kTok) / 16 / kPrepWaves;   // direct-to-LDS copies per wave
 static_assert(kCopiesPerChunk <= kCh / 16, "one copy after each run of products");
 constexpr int kMaxPairs = 64;             // channel pairs of a head (d <= 128)
 
@@ -95,18 +94,18 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
                  :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Copy i (0 <= i < kCopiesPerChunk) of copy wave `wave`'s share of input
-// channel chunk kc. The chunk is kRows/16 blocks of W' (the workgroup's
-// output channels; rows past the last head repeat it, never stored), then
-// kTok/16 blocks of X (rows past the last token repeat it, never stored),
-// each 16 rows x 64 bytes; copy wave w takes blocks j = kCopyWaves * i + w.
-// The 16-byte segment is swizzled by (row >> 1) & 3.
+// Copy i (0 <= i < kCopiesPerChunk) of wave `wave`'s share of input channel
+// chunk kc. The chunk is kRows/16 blocks of W' (the workgroup's output
+// channels; rows past the last head repeat it, never stored), then kTok/16
+// blocks of X (rows past the last token repeat it, never stored), each 16
+// rows x 64 bytes; wave w takes blocks j = kPrepWaves * i + w. The 16-byte
+// segment is swizzled by (row >> 1) & 3.
 __device__ __forceinline__ void issue_copy(unsigned stage, const unsigned char* Wrows, int nwrows,
                                            const unsigned char* Xrows, int ntok, int C, int kc,
                                            int wave, int lane, int i) {
     const int seg = lane & 3, rr = lane >> 2;
     const unsigned col = unsigned(kc * kKC) * 2 + 16 * (seg ^ ((lane >> 3) & 3));
-    const int j = kCopyWaves * i + wave;
+    const int j = kPrepWaves * i + wave;
     if (j < kRows / 16) {
         const int wrow = min(16 * j + rr, nwrows - 1);
         lds_copy16(stage + j * 1024, Wrows, unsigned(wrow) * unsigned(C) * 2 + col);
@@ -117,18 +116,17 @@ __device__ __forceinline__ void issue_copy(unsigned stage, const unsigned char* 
     }
 }
 
-// All of a copy wave's copies of chunk kc; other waves issue none.
+// All of a wave's copies of chunk kc.
 __device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows, int nwrows,
                                             const unsigned char* Xrows, int ntok, int C, int kc,
                                             int wave, int lane) {
-    if (wave >= kCopyWaves) return;
 #pragma unroll
     for (int i = 0; i < kCopiesPerChunk; ++i)
         issue_copy(stage, Wrows, nwrows, Xrows, ntok, C, kc, wave, lane, i);
 }
 
-// This wave's operands of one chunk: its 8 token granules of X and its head's
-// 8 channel blocks of W', each one 16-byte read per lane.
+// This wave's operands of one chunk: its G token granules of X and its head's
+// NB channel blocks of W', each one 16-byte read per lane.
 template <int G, int NB>
 __device__ __forceinline__ void load_operands(const unsigned char* S, int wr, int wc, int ka,
                                               bf16x8 (&xb)[G], bf16x8 (&wa)[NB]) {
@@ -240,7 +238,7 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
         const bool copies = steady || (k + 1 < nchunks && k + kStages < nchunks);
         const unsigned stage = smem_lds + (k % kStages) * kStage;
         products<G, NB>(xb[u], wa[u], acc, [&](int cb) {
-            if (copies && uwave < kCopyWaves && cb < kCopiesPerChunk)
+            if (copies && cb < kCopiesPerChunk)
                 issue_copy(stage, Wrows, nwrows, Xrows, ntok, p.C, k + kStages, uwave, lane, cb);
         });
     };
