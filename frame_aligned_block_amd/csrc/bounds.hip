@@ -108,7 +108,33 @@ __global__ __launch_bounds__(256) void bounds_colsum_qnorm(
     };
     if (JOINT) {
         const PartRows pr = part_rows(part, qp);
-        for (int r = pr.begin + r0; r < pr.end; r += RPI) {
+        int r = pr.begin + r0;
+        // four rows a trip, their loads issued together
+        for (; r + 3 * RPI < pr.end; r += 4 * RPI) {
+            Pack16<E> kk[4], qq[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kk[u] = load16(Kh + size_t(r + u * RPI) * D + lane * V);
+                qq[u] = load16(Qh + size_t(r + u * RPI) * D + lane * V);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[e] += float(kk[u].v[e]);
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float qe = float(qq[u].v[e]);
+                    ss = fmaf(qe, qe, ss);
+                }
+#pragma unroll
+                for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+                const float qn = sqrtf(ss);
+                qbest = fmaxf(qbest, qn);
+                if (lane == 0) qnorm[size_t(bh) * N + r + u * RPI] = qn;
+            }
+        }
+        for (; r < pr.end; r += RPI) {
             krow(r);
             qrow(r);
         }
@@ -170,7 +196,25 @@ __global__ __launch_bounds__(256) void bounds_radius(
 #pragma unroll
     for (int e = 0; e < V; ++e) m[e] = mu[size_t(bh) * D + lane * V + e];
     float best = 0.f;
-    for (int r = pr.begin + r0; r < pr.end; r += RPI) {
+    int r = pr.begin + r0;
+    for (; r + 3 * RPI < pr.end; r += 4 * RPI) {       // four rows a trip, loads together
+        Pack16<E> kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = load16(Kh + size_t(r + u * RPI) * D + lane * V);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float ce = float(kk[u].v[e]) - m[e];
+                ss = fmaf(ce, ce, ss);
+            }
+#pragma unroll
+            for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+            best = fmaxf(best, sqrtf(ss));
+        }
+    }
+    for (; r < pr.end; r += RPI) {
         const Pack16<E> k = load16(Kh + size_t(r) * D + lane * V);
         float ss = 0.f;
 #pragma unroll
