@@ -345,7 +345,17 @@ __global__ __launch_bounds__(256) void prep_rowscale(const __bf16* __restrict__ 
     if (row >= rows) return;                 // whole 16-lane groups: the shuffles stay in-group
     const __bf16* x = X + row * C;
     float s = 0.f;
-    for (int c = 8 * l; c < C; c += 128) {
+    int c = 8 * l;
+    for (; c + 3 * 128 < C; c += 4 * 128) {            // four loads a trip, issued together
+        bf16x8 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8*>(x + c + u * 128);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(float(v[u][e]), float(v[u][e]), s);
+    }
+    for (; c < C; c += 128) {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + c);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf(float(v[e]), float(v[e]), s);
@@ -411,7 +421,28 @@ __global__ __launch_bounds__(256) void prep_radius(const __bf16* __restrict__ K,
         acc[e] = 0.f;
     }
     float best = 0.f;
-    for (int r = begin + r0; r < end; r += RPI) {
+    auto krow = [&](const bf16x8& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ke = float(k[e]);
+            acc[e] += ke;
+            const float c = ke - m[e];
+            s = fmaf(c, c, s);
+        }
+#pragma unroll
+        for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+        best = fmaxf(best, sqrtf(s));
+    };
+    int r = begin + r0;
+    for (; r + 3 * RPI < end; r += 4 * RPI) {          // four rows a trip, loads together
+        bf16x8 kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = *reinterpret_cast<const bf16x8*>(Kh + size_t(r + u * RPI) * D + lane * 8);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) krow(kk[u]);
+    }
+    for (; r < end; r += RPI) {
         const bf16x8 k = *reinterpret_cast<const bf16x8*>(Kh + size_t(r) * D + lane * 8);
         float s = 0.f;
 #pragma unroll
