@@ -681,6 +681,10 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
 #pragma unroll
         for (int g = 0; g < G; ++g) mine[64 * i++] = m[g];
     }
+    // s_barrier does not wait for a wave's LDS writes on gfx950 (and the
+    // compiler adds no wait before a bare barrier): wait for them, or wave 0
+    // may read partials that have not landed.
+    FSA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     if (wave > 0) return false;
     for (int w = 1; w < fsa::kWaves; ++w) {

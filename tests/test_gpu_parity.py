@@ -327,3 +327,23 @@ def test_attention_entry_point():
     assert_close(cfg, O[0, 3, rows], want, "fsa_attention")
     run.bounds()
     assert torch.equal(run.forward(), O)
+
+
+def test_split_workgroups_exact_and_deterministic():
+    """T = 3600 leaves each frame's last workgroup a single row unit, which
+    its four waves split over the key chunks and then combine through LDS.
+    Every row of those units, in every frame and head, on both routes, against
+    the oracle; and three launches of each route bit-identical (a combine that
+    read partials before they landed would show in both)."""
+    cfg = CONFIGS["720p"].with_(F=5, H=4)
+    say("split workgroups", cfg.name)
+    run = Run(cfg).bounds()
+    rows = np.concatenate([np.arange(f * cfg.T + 3584, (f + 1) * cfg.T) for f in range(cfg.F)])
+    for mode in ("auto", "online"):
+        outs = [run.forward(mode) for _ in range(3)]
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0]), mode
+        for h in range(cfg.H):
+            want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
+            mx, mean = assert_close(cfg, outs[0][0, h, rows], want, f"split rows {mode} head {h}")
+            print(f"split rows {mode} h{h}: max {mx:.3g} mean {mean:.3g}")
