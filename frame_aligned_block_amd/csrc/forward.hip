@@ -311,8 +311,13 @@ __device__ __forceinline__ float sum_pairs(const bf16x2* pp, int n, float acc) {
 }
 
 // Probabilities of NK scores of one granule-row. Fixed route: the shift is
-// the row's Cauchy-Schwarz bound. Online route: the running max, with the
-// accumulator and row sum rescaled when it grows.
+// the row's Cauchy-Schwarz bound. Online route: a running reference max,
+// moved (with the accumulator and row sum rescaled) only when a step's max
+// exceeds it by more than kLazyLog2 in log2 units, and only in the steps
+// where some row of the wave needs it; until then the row's probabilities
+// may reach 2^kLazyLog2, which bf16 and the fp32 sums hold as precisely.
+constexpr float kLazyLog2 = 8.f;
+
 template <int D, int G, bool FIXED, int NK>
 __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const float (&shift)[G],
                                       float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
@@ -327,13 +332,16 @@ __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const flo
         for (int i = 1; i < NK; ++i) mx = fmaxf(mx, sv[i >> 2][i & 3]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[g], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m[g] - mnew) * c);
-        m[g] = mnew;
-        rs[g] *= alpha;
+        const bool grow = (mx - m[g]) * c > kLazyLog2;          // always at the first step
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {           // uniform
+            const float mnew = grow ? mx : m[g];
+            const float alpha = __builtin_amdgcn_exp2f((m[g] - mnew) * c);
+            m[g] = mnew;
+            rs[g] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[g][db] *= alpha;
-        const float sh = mnew * c;
+            for (int db = 0; db < D / 16; ++db) o[g][db] *= alpha;
+        }
+        const float sh = m[g] * c;
 #pragma unroll
         for (int i = 0; i < NK; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -sh));
     }
