@@ -9,6 +9,8 @@ size instead of a window. The shapes cover single frames, frames shorter than
 one workgroup, spans that leave ragged row units and key chunks, and both
 kernels' head widths.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -42,7 +44,12 @@ def draw_case(i: int):
     return cfg, str(rng.choice(MODES))
 
 
-@pytest.mark.parametrize("i", range(24))
+# FSA_FUZZ_CASES widens the sweep for a one-off run (the default keeps the
+# suite short)
+N_CASES = int(os.environ.get("FSA_FUZZ_CASES", "24"))
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape(i):
     cfg, mode = draw_case(i)
     say("fuzz", i, cfg, mode)
