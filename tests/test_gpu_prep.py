@@ -10,6 +10,8 @@ the row norms and key mean against the GPU's own bf16 outputs in fp64
 (1e-5 relative); the bounds products as for fsa_bounds, flags bit-exact; the
 attention fed by the producer against the oracle on the same tensors.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -211,7 +213,11 @@ def draw_prep_case(i: int):
                 window=int(rng.integers(1, 3)), ref=int(rng.integers(0, F)))
 
 
-@pytest.mark.parametrize("i", range(8))
+# FSA_PREP_FUZZ_CASES widens the sweep for a one-off run
+N_PREP_CASES = int(os.environ.get("FSA_PREP_FUZZ_CASES", "8"))
+
+
+@pytest.mark.parametrize("i", range(N_PREP_CASES))
 def test_prep_random_shapes(i):
     """Random grids, frame counts, head counts (an odd head count leaves a
     workgroup's second head empty), batches, windows and reference frames:
