@@ -13,17 +13,25 @@
 //  * "Proving the Pixels Didn't Change" ¶2: P enters the P.V product in bf16.
 //
 // gfx950 design (bf16):
-//  * A workgroup is 4 waves; each wave owns 16*G consecutive query rows of one
-//    frame, and the 4 waves of a workgroup own consecutive row units of the
-//    same frame, so they share one key slice. The slice is at most two
-//    contiguous token runs (the clipped window, and the reference frame when
-//    it lies outside it), read from a per-frame table passed as a kernel
-//    argument. The runs are walked as one sequence in chunks of 64 keys; only
-//    the very last chunk can be shorter (16, 32 or 48 keys, a whole number of
-//    16-key granules, so still no partial block).
-//  * Per chunk, K and V are staged in LDS by direct-to-LDS copies, double
-//    buffered with one barrier per chunk; the V^T operand of P.V is read
-//    transposed out of row-major V (ds_read_b64_tr_b16).
+//  * Each wave owns 16*G consecutive query rows of one frame (a row unit); the
+//    waves of a workgroup own consecutive row units of the same frame, so they
+//    share one key slice. The slice is at most two contiguous token runs (the
+//    clipped window, and the reference frame when it lies outside it), read
+//    from a per-frame table passed as a kernel argument. The runs are walked
+//    as one sequence in chunks of 64 keys; only the very last chunk can be
+//    shorter (16, 32 or 48 keys, a whole number of 16-key granules, so still
+//    no partial block).
+//  * Two workgroup geometries, chosen per shape by the plan:
+//    - 8 waves (256 rows), one workgroup per CU: K and V chunks stream into a
+//      4-stage LDS ring by direct-to-LDS copies, shared by all 8 waves, with
+//      one barrier per pair of chunks; the copies of the pair after next are
+//      issued right after each barrier;
+//    - 4 waves (128 rows), two workgroups per CU: a 2-stage ring with one
+//      barrier per chunk (used where a frame's rows fill 256-row workgroups
+//      poorly, and for the split walk of a frame's last single unit).
+//    In both, the V^T operand of P.V is read transposed out of row-major V
+//    (ds_read_b64_tr_b16), and two waves share each SIMD so that one wave's
+//    softmax runs while the other's products occupy the matrix unit.
 //  * Both routes score K as given. The fixed route's shift for row i is its
 //    bound on the centred scores, scale ||q_i|| R_S, plus scale q_i.mu:
 //    centring moves every score of the row by that amount, so the softmax is
@@ -159,11 +167,7 @@ __device__ __forceinline__ int pair_at(const FwdArgs& p, int ti, bool mixed) {
 
 // ---------------------------------------------------------------- bf16 route
 
-#ifndef FSA_CHUNK_KEYS
-#define FSA_CHUNK_KEYS 64
-#endif
-constexpr int kBK = FSA_CHUNK_KEYS;  // keys per LDS chunk; two chunks in LDS
-static_assert(kBK == 32 || kBK == 64 || kBK == 128, "chunk of 32, 64 or 128 keys");
+constexpr int kBK = 64;                 // keys per LDS chunk
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -177,6 +181,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //    (chosen by measuring SQ_LDS_BANK_CONFLICT over candidate swizzles);
 //  * V (read transposed, 4 rows x 32 bytes per 16 lanes): 32-byte half
 //    ^= (row >> 2) & 1.
+// A tile is copied as 1 KB blocks of 16 rows x 64 bytes: block j is sub-tile
+// j / RB, rows 16 (j % RB) .. +15.
 template <int D>
 struct Geo {
     static constexpr int KS = D / 32;                  // k-steps of S^T over d = sub-tiles
@@ -185,8 +191,7 @@ struct Geo {
     static constexpr int TILE = KS * SUB;              // one K (or V) chunk
     static constexpr int STAGE = 2 * TILE;             // K tile, then V tile
     static constexpr int RB = kBK / 16;                // 16-row blocks per sub-tile
-    static constexpr int NI = KS * RB / fsa::kWaves;   // 1 KB copies per wave per tile
-    static constexpr int LOADS = 2 * NI;               // wave copies per chunk (K and V)
+    static constexpr int BLOCKS = KS * RB;             // 1 KB blocks per tile
 };
 
 // vmcnt(n) with no wait on the other counters (gfx9 encoding).
@@ -205,46 +210,53 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
 }
 
 // Asynchronous global -> LDS copies of chunk ch of the slice walk (K and V
-// straight into the stage, no registers). The tile's 1 KB blocks (16 rows x
-// 64 bytes of one sub-tile) are numbered j = 4i + w for the block groups
-// i < NI and the workgroup's waves w; block j is sub-tile j / RB, rows
-// 16 (j % RB) .. +15, so the blocks of w always hold the same 16 rows: lane l
-// carries row 16 (w % RB) + l/4, 16-byte segment l%4. Positions past the
-// slice are clamped to its last key: harmless duplicates that are never read.
-// issue_group issues group i of the blocks of w: one K and one V copy.
-template <int D>
+// straight into the stage, no registers). A workgroup of W waves numbers the
+// tile's 1 KB blocks j = W i + w for the block groups i < BLOCKS / W and its
+// waves w; W is a multiple of RB, so the blocks of w always hold the same 16
+// rows: lane l carries row 16 (w % RB) + l/4, 16-byte segment l%4. Positions
+// past the slice are clamped to its last key: harmless duplicates that are
+// never read. issue_group issues group i of the blocks of w: one K and one V
+// copy.
+template <int D, int W>
 __device__ __forceinline__ void issue_group(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                             const __bf16* Vh, int ch, int wave, int lane, int i) {
     using GG = Geo<D>;
+    static_assert(W % GG::RB == 0 && GG::BLOCKS % W == 0, "waves tile the blocks");
     const int row = 16 * (wave % GG::RB) + (lane >> 2);
     const unsigned rowoff = unsigned(sl.key(min(ch * kBK + row, sl.total - 1))) * (2 * D);
     const int seg = lane & 3;
     const unsigned koff = rowoff + 16 * (seg ^ ((lane >> 3) & 3));     // (row >> 1) & 3
     const unsigned voff = rowoff + 16 * (seg ^ (((lane >> 4) & 1) << 1));
-    const int j = i * fsa::kWaves + wave;
+    const int j = i * W + wave;
     const int t = j / GG::RB;                          // sub-tile = 32-column block
     const unsigned dst = stage_lds + t * GG::SUB + (j % GG::RB) * 1024;
     lds_copy16(dst, reinterpret_cast<const unsigned char*>(Kh) + 64 * t, koff);
     lds_copy16(dst + GG::TILE, reinterpret_cast<const unsigned char*>(Vh) + 64 * t, voff);
 }
 
-// A whole chunk's copies, issued by the first kCopyWaves waves of the
-// workgroup (wave w < kCopyWaves also issues the groups of waves w +
-// kCopyWaves, ...). A wave that issues copies stalls while the CU's address
-// path takes them; two copying waves measured about 1% faster than all four
-// (the others start their next step at once) and than one (too long a stall).
-constexpr int kCopyWaves = fsa::kWaves >= 2 ? 2 : 1;
-static_assert(fsa::kWaves % kCopyWaves == 0, "copy waves divide the workgroup");
-
+// 4-wave workgroups: a whole chunk's copies, issued by the first two waves
+// (wave w < 2 also issues the groups of wave w + 2). A wave that issues
+// copies stalls while the CU's address path takes them; two copying waves
+// measured about 1% faster than all four (the others start their next step
+// at once) and than one (too long a stall).
 template <int D>
-__device__ __forceinline__ void issue_chunk(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
-                                            const __bf16* Vh, int ch, int wave, int lane) {
-    if (wave >= kCopyWaves) return;
+__device__ __forceinline__ void issue_chunk4(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
+                                             const __bf16* Vh, int ch, int wave, int lane) {
+    if (wave >= 2) return;
 #pragma unroll
-    for (int r = 0; r < fsa::kWaves / kCopyWaves; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int i = 0; i < Geo<D>::NI; ++i)
-            issue_group<D>(stage_lds, sl, Kh, Vh, ch, wave + r * kCopyWaves, lane, i);
+        for (int i = 0; i < Geo<D>::BLOCKS / 4; ++i)
+            issue_group<D, 4>(stage_lds, sl, Kh, Vh, ch, wave + 2 * r, lane, i);
+}
+
+// 8-wave workgroups: every wave issues its own groups of the chunk.
+template <int D>
+__device__ __forceinline__ void issue_chunk8(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
+                                             const __bf16* Vh, int ch, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < Geo<D>::BLOCKS / 8; ++i)
+        issue_group<D, 8>(stage_lds, sl, Kh, Vh, ch, wave, lane, i);
 }
 
 // Per-lane LDS byte offsets (constant for the whole walk).
@@ -462,14 +474,10 @@ __device__ __forceinline__ void pv_half(const unsigned char* Vs, int koff, const
 // lgkmcnt(0) with no wait on the other counters (gfx9 encoding).
 #define FSA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4))
 
-#ifndef FSA_PRIO
-#define FSA_PRIO 1
-#endif
-// Issue priority of the vector phase (FSA_PRIO 1) or of the matrix phase (2).
-__device__ __forceinline__ void prio_vector_begin() { if (FSA_PRIO == 1) __builtin_amdgcn_s_setprio(1); }
-__device__ __forceinline__ void prio_vector_end() { if (FSA_PRIO == 1) __builtin_amdgcn_s_setprio(0); }
-__device__ __forceinline__ void prio_matrix_begin() { if (FSA_PRIO == 2) __builtin_amdgcn_s_setprio(1); }
-__device__ __forceinline__ void prio_matrix_end() { if (FSA_PRIO == 2) __builtin_amdgcn_s_setprio(0); }
+// The vector phase of a step runs at issue priority 1 (measured neutral to
+// slightly faster than none, or than raising the matrix phase instead).
+__device__ __forceinline__ void prio_vector_begin() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_vector_end() { __builtin_amdgcn_s_setprio(0); }
 
 // The slice walk of one workgroup. Each 32-key step t runs in two phases: a
 // vector phase (the softmax of S_t, while this step's V operands and the next
@@ -499,10 +507,10 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
 
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
-    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    issue_chunk4<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
     FSA_WAIT_VMCNT(0);                                  // chunk 0 has landed
     __builtin_amdgcn_s_barrier();
-    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
+    if (nchunks > 1) issue_chunk4<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
 
     f32x4 sv[2][G];
     scores<D, G, 2>(smem, 0, qf, sv, la);
@@ -521,7 +529,7 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
                 FSA_WAIT_LGKM0();                       // this step's V is in registers
                 __builtin_amdgcn_s_barrier();
                 if (FIXED && ch + 2 < nchunks)
-                    issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+                    issue_chunk4<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
                 st ^= 1;
                 load_k<D>(smem + st * GG::STAGE, 0, ka, la);
             }
@@ -530,7 +538,6 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
             softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
             prio_vector_end();
             __builtin_amdgcn_sched_barrier(0);
-            prio_matrix_begin();
             if (!FIXED && s + 1 == SPC) {
                 // Online route: the copies of the chunk after next are issued
                 // between the k-steps of the matrix phase, which measured faster
@@ -538,14 +545,14 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
                 // route is faster the other way). Past the last chunk they
                 // repeat the slice's last key into the free stage, never read.
                 const unsigned dst = smem_lds + (st ^ 1) * GG::STAGE;
-                static_assert(GG::NI <= GG::KS, "one copy group per k-step");
+                constexpr int NI = GG::BLOCKS / 4;
+                static_assert(NI <= GG::KS, "one copy group per k-step");
                 qk_pv<D, G>(ka, qf, sv, va, pk, o, [&](int ks) {
-                    if (ks < GG::NI) issue_group<D>(dst, sl, Kh, Vh, ch + 2, wave, lane, ks);
+                    if (ks < NI) issue_group<D, 4>(dst, sl, Kh, Vh, ch + 2, wave, lane, ks);
                 });
             } else {
                 qk_pv<D, G>(ka, qf, sv, va, pk, o);
             }
-            prio_matrix_end();
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -588,25 +595,138 @@ __device__ __forceinline__ void copy_only(unsigned char* smem, const Slice& sl, 
     using GG = Geo<D>;
     const int nchunks = (sl.total + kBK - 1) / kBK;
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
-    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    issue_chunk4<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
     FSA_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
+    if (nchunks > 1) issue_chunk4<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
     int st = 0;
     for (int ch = 0; ch + 1 < nchunks; ++ch) {
         FSA_WAIT_VMCNT(0);
         __builtin_amdgcn_s_barrier();
         if (ch + 2 < nchunks) {
             if (fixed) {
-                issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+                issue_chunk4<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
             } else {
 #pragma unroll
-                for (int i = 0; i < GG::NI; ++i)
-                    issue_group<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane, i);
+                for (int i = 0; i < GG::BLOCKS / 4; ++i)
+                    issue_group<D, 4>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane, i);
             }
         }
         st ^= 1;
     }
+    FSA_WAIT_VMCNT(0);
+}
+
+// An empty asm statement that may touch any memory: LDS reads are neither
+// hoisted above nor sunk below it (a barrier alone does not order them).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// The slice walk of an 8-wave workgroup (256 rows, one workgroup per CU, so
+// the two waves of each SIMD belong to the same workgroup). Chunks of kBK
+// keys stream into a 4-stage LDS ring; every wave copies its own blocks of
+// every chunk, and the waves meet at one barrier per pair of chunks. A
+// microbenchmark of this step's instruction mix measured that well ahead of a
+// barrier per chunk: each barrier lines up the two waves of a SIMD, and only
+// between barriers do their vector and matrix phases drift apart and overlap.
+// Chunk c lives in stage c % 4. Before the walk, chunks 0-3 are issued, 0 and
+// 1 have landed, and the waves pass one barrier. Barrier p sits in step
+// 4p + 3 (the last step of chunks 2p and 2p + 1), between that step's V reads
+// and the next step's K reads. Before it each wave waits for its own copies
+// (chunks 2p + 2 and 2p + 3, issued at barrier p - 1) and for its own reads,
+// so after it chunks 2p + 2 and 2p + 3 are visible to every wave and no wave
+// reads the stages of chunks 2p and 2p + 1 again: the copies of chunks 2p + 4
+// and 2p + 5 go there at once. The steps themselves are those of attend.
+template <int D>
+__device__ __forceinline__ void walk8_prologue(unsigned lds0, const Slice& sl, const __bf16* Kh,
+                                               const __bf16* Vh, int nchunks, int wave, int lane) {
+    using GG = Geo<D>;
+    constexpr int CPW = 2 * (GG::BLOCKS / 8);          // copies per wave per chunk
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+        if (ch < nchunks) issue_chunk8<D>(lds0 + ch * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
+    // chunks 0 and 1 have landed; 2 and 3 may still be in flight
+    if (nchunks >= 4) FSA_WAIT_VMCNT(2 * CPW);
+    else if (nchunks == 3) FSA_WAIT_VMCNT(CPW);
+    else FSA_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+template <int D>
+__device__ __forceinline__ void walk8_barrier(unsigned lds0, const Slice& sl, const __bf16* Kh,
+                                              const __bf16* Vh, int pair, int nchunks, int wave,
+                                              int lane) {
+    using GG = Geo<D>;
+    compiler_fence();
+    FSA_WAIT_VMCNT(0);                                  // my copies of chunks 2p+2, 2p+3
+    FSA_WAIT_LGKM0();                                   // my reads of chunks 2p, 2p+1
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+#pragma unroll
+    for (int ch = 2 * pair + 4; ch < 2 * pair + 6; ++ch)
+        if (ch < nchunks) issue_chunk8<D>(lds0 + (ch & 3) * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
+}
+
+template <int D, int G, bool FIXED>
+__device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, const __bf16* Kh,
+                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
+                                        const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
+                                        float (&rs)[G], int wave, int lane) {
+    using GG = Geo<D>;
+    const LaneAddr la = lane_addr(lane & 15, lane >> 4);
+    const int nchunks = (sl.total + kBK - 1) / kBK;
+    const int nsteps = (sl.total + 31) >> 5;
+    float m[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+    const unsigned lds0 = unsigned(uintptr_t((lds_void*)smem));
+    walk8_prologue<D>(lds0, sl, Kh, Vh, nchunks, wave, lane);
+
+    f32x4 sv[2][G];
+    scores<D, G, 2>(smem, 0, qf, sv, la);
+    for (int t = 0; t + 1 < nsteps; ++t) {
+        const unsigned char* S0 = smem + ((t >> 1) & 3) * GG::STAGE;
+        bf16x8 va[GG::DB];
+        load_v<D>(S0 + GG::TILE, 32 * (t & 1), va, la);
+        if ((t & 3) == 3) walk8_barrier<D>(lds0, sl, Kh, Vh, t >> 2, nchunks, wave, lane);
+        const int t1 = t + 1;
+        bf16x8 ka[GG::KS][2];
+        load_k<D>(smem + ((t1 >> 1) & 3) * GG::STAGE, 32 * (t1 & 1), ka, la);
+        bf16x2 pk[G][4];
+        prio_vector_begin();
+        softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+        prio_vector_end();
+        __builtin_amdgcn_sched_barrier(0);
+        qk_pv<D, G>(ka, qf, sv, va, pk, o);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // The last step: 32 keys, or the slice's lone last 16-key granule.
+    const int t = nsteps - 1;
+    const unsigned char* S0 = smem + ((t >> 1) & 3) * GG::STAGE;
+    if (sl.total - 32 * t >= 32) {
+        bf16x8 va[GG::DB];
+        load_v<D>(S0 + GG::TILE, 32 * (t & 1), va, la);
+        bf16x2 pk[G][4];
+        softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+        pv<D, G>(va, pk, o);
+    } else {
+        bf16x2 pk[G][2];
+        softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+        pv_half<D, G>(S0 + GG::TILE, 32 * (t & 1), pk, o, la);
+    }
+    FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
+}
+
+// A wave of an 8-wave workgroup that owns no query rows: the same copies and
+// barriers as attend8, in the same order, with no matrix or softmax work.
+template <int D>
+__device__ __forceinline__ void copy_only8(unsigned char* smem, const Slice& sl, const __bf16* Kh,
+                                           const __bf16* Vh, int wave, int lane) {
+    const int nchunks = (sl.total + kBK - 1) / kBK;
+    const int nsteps = (sl.total + 31) >> 5;
+    const unsigned lds0 = unsigned(uintptr_t((lds_void*)smem));
+    walk8_prologue<D>(lds0, sl, Kh, Vh, nchunks, wave, lane);
+    for (int t = 3; t + 1 < nsteps; t += 4) walk8_barrier<D>(lds0, sl, Kh, Vh, t >> 2, nchunks, wave, lane);
     FSA_WAIT_VMCNT(0);
 }
 
@@ -629,10 +749,10 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
     const unsigned smem_lds = unsigned(uintptr_t((lds_void*)smem));
-    issue_chunk<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
+    issue_chunk4<D>(smem_lds, sl, Kh, Vh, 0, wave, lane);
     FSA_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
-    if (nchunks > 1) issue_chunk<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
+    if (nchunks > 1) issue_chunk4<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
     int st = 0;
     for (int ch = 0; ch < nchunks; ++ch) {
         if (ch * kBK + 16 * wave < sl.total) {                  // this wave's granule exists
@@ -650,7 +770,7 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
             FSA_WAIT_LGKM0();                                   // no read of the old stage is pending
             __builtin_amdgcn_s_barrier();
             if (ch + 2 < nchunks)
-                issue_chunk<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
+                issue_chunk4<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
             st ^= 1;
         }
     }
@@ -662,7 +782,7 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
 template <int D, int G>
 constexpr int split_floats() { return G * (D / 16) * 4 + 2 * G; }
 
-// Adds the partial results of a split workgroup's waves into wave 0, in
+// Adds the partial results of a split (4-wave) workgroup's waves into wave 0, in
 // wave order (so the sum is deterministic), through the LDS the key ring used.
 // The fixed route's partial sums share one shift and simply add; the online
 // route rescales each to the largest running max first. Returns true in wave
@@ -695,7 +815,7 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
     FSA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     if (wave > 0) return false;
-    for (int w = 1; w < fsa::kWaves; ++w) {
+    for (int w = 1; w < 4; ++w) {
         const float* theirs = buf + (w - 1) * NF * 64 + lane;
         constexpr int RS = G * (D / 16) * 4, MX = RS + G;
         if (fixed) {
@@ -728,19 +848,23 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
     return true;
 }
 
-// Workgroups per CU for two waves per SIMD (<= 256 registers per lane) while
-// a wave's accumulators and query fragments fit, else one wave per SIMD.
-constexpr int fwd_occupancy(int D, int G) {
-    return G * D <= 256 ? (2 * 4 / fsa::kWaves > 0 ? 2 * 4 / fsa::kWaves : 1) : 1;
+// LDS of a workgroup: the key ring (4 stages for 8 waves, 2 for 4 waves); a
+// split 4-wave workgroup reuses it to combine its waves' partials.
+template <int D, int G, int W>
+constexpr int fwd_lds_bytes() {
+    return W == 8 ? 4 * Geo<D>::STAGE
+                  : (2 * Geo<D>::STAGE > 3 * split_floats<D, G>() * 64 * 4
+                         ? 2 * Geo<D>::STAGE : 3 * split_floats<D, G>() * 64 * 4);
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(const FwdArgs p) {
+// W waves of 16*G rows each; two waves per SIMD (<= 256 registers per lane):
+// two 4-wave workgroups or one 8-wave workgroup per CU.
+template <int D, int G, int W>
+__global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
     using GG = Geo<D>;
-    // the key ring; a split workgroup reuses it to combine its waves' partials
-    constexpr int kSplitBytes = (fsa::kWaves - 1) * split_floats<D, G>() * 64 * 4;
-    __shared__ __attribute__((aligned(16)))
-        unsigned char smem[2 * GG::STAGE > kSplitBytes ? 2 * GG::STAGE : kSplitBytes];
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
+    static_assert(G * D <= 256, "a wave's accumulators and query fragments fit 256 registers");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[fwd_lds_bytes<D, G, W>()];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ln = lane & 15, lj = lane >> 4;
@@ -764,11 +888,11 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
     // frame (the tail of a frame whose granule count G does not divide)
     // repeat the frame's last granule and are not stored: every computing
     // wave runs the same loop, with no predicate inside it. A wave wholly
-    // past the last unit only helps stage the keys, except in a workgroup
-    // left with a single unit: there every wave takes that unit and a share
-    // of the key chunks (attend_split).
-    const int first_unit = gq * fsa::kWaves;
-    const bool split = kBK == 16 * fsa::kWaves && p.units_per_frame - first_unit == 1;   // uniform
+    // past the last unit only helps stage the keys, except in a 4-wave
+    // workgroup left with a single unit: there every wave takes that unit and
+    // a share of the key chunks (attend_split).
+    const int first_unit = gq * W;
+    const bool split = W == 4 && p.units_per_frame - first_unit == 1;   // uniform
     const int unit = split ? first_unit : first_unit + wave;
     const int ngran = T >> 4;
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
@@ -778,7 +902,7 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
         // The workgroup takes the fixed max iff every one of its rows has its
         // gap bound ||q_i|| R_S - q_i.dslice within the limit: each wave
         // reduces its rows, the waves meet once in LDS (idle waves too).
-        __shared__ float wave_gap[fsa::kWaves];
+        __shared__ float wave_gap[W];
         float g = -INFINITY;
         if (!idle) {
             const float rsl = p.rslice[size_t(bh) * p.F + f];
@@ -804,11 +928,12 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
         __syncthreads();
         float wg = wave_gap[0];
 #pragma unroll
-        for (int w = 1; w < fsa::kWaves; ++w) wg = fmaxf(wg, wave_gap[w]);
+        for (int w = 1; w < W; ++w) wg = fmaxf(wg, wave_gap[w]);
         fixed = row_gap_ok(wg, p.c);
     }
     if (idle) {
-        copy_only<D>(smem, sl, Kh, Vh, fixed, uwave, lane);
+        if (W == 8) copy_only8<D>(smem, sl, Kh, Vh, uwave, lane);
+        else copy_only<D>(smem, sl, Kh, Vh, fixed, uwave, lane);
         return;
     }
     const float c = p.c;
@@ -850,7 +975,10 @@ __global__ __launch_bounds__(fsa::kThreads, fwd_occupancy(D, G)) void fwd_bf16(c
 #pragma unroll
     for (int g = 0; g < G; ++g) shift[g] *= c;
 
-    if (split) {
+    if (W == 8) {
+        if (fixed) attend8<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+        else attend8<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+    } else if (split) {
         float m[G];
         if (fixed)
             attend_split<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
@@ -943,9 +1071,9 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
     for (int e = 0; e < D; ++e) Oh[size_t(i) * D + e] = o[e] * inv;
 }
 
-template <int D, int G>
+template <int D, int G, int W>
 void launch_bf16(const FwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_bf16<D, G>), dim3(a.nwg), dim3(fsa::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16<D, G, W>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
 }
 
 }  // namespace
@@ -993,13 +1121,17 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
             return FSA_ERR_UNSUPPORTED;
         }
         a.nwg = int32_t(p.forward.workgroups);
-        const int G = p.forward.granules;
-        if (s.d == 128 && G == 2) {
-            launch_bf16<128, 2>(a, stream);
-        } else if (s.d == 64 && G == 4) {
-            launch_bf16<64, 4>(a, stream);
+        const int G = p.forward.granules, W = p.forward.waves;
+        if (s.d == 128 && G == 2 && W == 8) {
+            launch_bf16<128, 2, 8>(a, stream);
+        } else if (s.d == 128 && G == 2 && W == 4) {
+            launch_bf16<128, 2, 4>(a, stream);
+        } else if (s.d == 64 && G == 2 && W == 8) {
+            launch_bf16<64, 2, 8>(a, stream);
+        } else if (s.d == 64 && G == 2 && W == 4) {
+            launch_bf16<64, 2, 4>(a, stream);
         } else {
-            set_error("fsa_forward: no kernel for d=%d with %d granules per wave", s.d, G);
+            set_error("fsa_forward: no kernel for d=%d with %d granules and %d waves", s.d, G, W);
             return FSA_ERR_UNSUPPORTED;
         }
     }

@@ -25,14 +25,6 @@ struct FrameTable {
     uint32_t order[(FSA_MAX_FRAMES + 4) / 4];
 };
 
-// Query rows per wave = 16 * granules; a workgroup holds kWaves waves of
-// consecutive row units of one frame.
-#ifndef FSA_WAVES
-#define FSA_WAVES 4
-#endif
-constexpr int kWaves = FSA_WAVES;
-constexpr int kThreads = 64 * kWaves;
-
 // Rows of one side (queries or keys) cut into parts of at most 256 rows
 // that never straddle a frame of that side.
 struct Parts {
@@ -51,12 +43,19 @@ struct BoundsGeometry {
     size_t partqmax;          // float [BH][q parts]: max ||q_i|| per part
 };
 
+// The bf16 forward kernel's launch: workgroups of `waves` waves (4 or 8),
+// each wave a unit of 16 * granules consecutive query rows of one frame, the
+// waves of a workgroup consecutive units of the same frame.
 struct ForwardGeometry {
+    int32_t waves;             // waves per workgroup: 4 or 8
     int32_t granules;          // 16-row granules per wave
     int32_t units_per_frame;   // ceil(T / (16 * granules)); the last may be partial
-    int32_t groups_per_frame;  // ceil(units_per_frame / kWaves)
+    int32_t groups_per_frame;  // ceil(units_per_frame / waves)
     int64_t workgroups;        // B * H * F * groups_per_frame
 };
+
+// Fill the forward geometry of a plan for `waves` waves per workgroup.
+void set_forward_geometry(fsa_plan& p, int32_t waves);
 
 }  // namespace fsa
 

@@ -33,9 +33,25 @@ int32_t pick_bq(int32_t T) {
 }
 
 // 16-row granules per wave of the bf16 forward kernel: what two waves per
-// SIMD can hold in registers (output accumulators plus query fragments).
-int32_t kernel_granules(int32_t d) { return d == 128 ? 2 : 4; }
+// SIMD can hold in registers (output accumulators plus query fragments) at
+// d = 128; d = 64 keeps the same 32 rows per wave.
+constexpr int32_t kGranules = 2;
 
+// Waves per workgroup of the bf16 forward kernel. 4-wave workgroups (128
+// rows, two per CU): the two waves that share a SIMD belong to different
+// workgroups, so one workgroup's barrier never lines them up, and one wave's
+// softmax keeps overlapping the other's products. 8-wave workgroups (256 rows,
+// one per CU) share each chunk's copies among twice the rows, but their
+// barriers align both waves of every SIMD; measured slower on every workload
+// (720p 9.41 against 8.98 ms, 1080p 21.3 against 20.3 ms, same process), so
+// they are chosen only on request (fsa_plan_set_row_block).
+int32_t pick_waves(const fsa_shape& s) {
+    (void)s;
+    return 4;
+}
+
+// k-block size of the tile list when the caller leaves it open: as pick_bq,
+// over the key frame's span.
 int32_t pick_bk(int32_t T) {
     int32_t n = T / 16;
     for (int32_t g = 4; g >= 1; --g)
@@ -196,13 +212,8 @@ fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const c
         for (int32_t f = 0; f < s.F; ++f) total += p->slice_size[f];
         p->valid_pairs = total * int64_t(s.T) * KT;
 
-        // ---- forward geometry: each wave takes `granules` consecutive 16-row
-        // granules of one frame; a frame's last unit may hold fewer.
-        const int32_t granules = kernel_granules(s.d);
-        p->forward.granules = granules;
-        p->forward.units_per_frame = (s.T / 16 + granules - 1) / granules;
-        p->forward.groups_per_frame = (p->forward.units_per_frame + kWaves - 1) / kWaves;
-        p->forward.workgroups = int64_t(s.B) * s.H * s.F * p->forward.groups_per_frame;
+        // ---- forward geometry
+        set_forward_geometry(*p, pick_waves(s));
 
         // ---- bounds geometry: parts never straddle a frame of their side
         p->bounds.q = make_parts(s.F, s.T);
@@ -241,6 +252,21 @@ fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const c
 }
 
 }  // namespace
+
+namespace fsa {
+
+// Each wave takes `granules` consecutive 16-row granules of one frame; a
+// frame's last unit may hold fewer, and its last workgroup fewer units.
+void set_forward_geometry(fsa_plan& p, int32_t waves) {
+    ForwardGeometry& g = p.forward;
+    g.waves = waves;
+    g.granules = kGranules;
+    g.units_per_frame = (p.shape.T / 16 + kGranules - 1) / kGranules;
+    g.groups_per_frame = (g.units_per_frame + waves - 1) / waves;
+    g.workgroups = int64_t(p.shape.B) * p.shape.H * p.shape.F * g.groups_per_frame;
+}
+
+}  // namespace fsa
 
 extern "C" fsa_status fsa_plan_create(const fsa_shape* shape, fsa_plan** out) {
     return create_plan(shape, 0, out, "fsa_plan_create");
@@ -300,5 +326,36 @@ extern "C" fsa_status fsa_workspace_layout(const fsa_plan* plan, fsa_ws_layout* 
         return FSA_ERR_INVALID_ARG;
     }
     *out = plan->ws;
+    return FSA_OK;
+}
+
+extern "C" int32_t fsa_plan_row_block(const fsa_plan* plan) {
+    if (!plan) return -1;
+    if (plan->shape.dtype == FSA_F32) return 1;
+    return 16 * plan->forward.granules * plan->forward.waves;
+}
+
+extern "C" fsa_status fsa_plan_set_row_block(fsa_plan* plan, int32_t rows) {
+    if (!plan) {
+        fsa::set_error("fsa_plan_set_row_block: NULL plan");
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (plan->shape.dtype == FSA_F32) {
+        if (rows == 0 || rows == 1) return FSA_OK;
+        fsa::set_error("fsa_plan_set_row_block: an fp32 plan computes one row per thread "
+                       "(rows must be 0 or 1, got %d)", rows);
+        return FSA_ERR_INVALID_ARG;
+    }
+    const int32_t per_wave = 16 * kGranules;
+    int32_t waves;
+    if (rows == 0) waves = pick_waves(plan->shape);
+    else if (rows == 4 * per_wave) waves = 4;
+    else if (rows == 8 * per_wave) waves = 8;
+    else {
+        fsa::set_error("fsa_plan_set_row_block: rows must be 0, %d or %d, got %d", 4 * per_wave,
+                       8 * per_wave, rows);
+        return FSA_ERR_INVALID_ARG;
+    }
+    fsa::set_forward_geometry(*plan, waves);
     return FSA_OK;
 }

@@ -46,7 +46,8 @@ FSA_MAX_FRAMES = 255
 # Every symbol include/fsa.h declares.
 EXPORTS = (
     "fsa_plan_create", "fsa_plan_create_cross", "fsa_plan_destroy", "fsa_plan_shape",
-    "fsa_plan_export", "fsa_plan_valid_pairs", "fsa_plan_key_tokens", "fsa_workspace_bytes",
+    "fsa_plan_export", "fsa_plan_valid_pairs", "fsa_plan_key_tokens", "fsa_plan_row_block",
+    "fsa_plan_set_row_block", "fsa_workspace_bytes",
     "fsa_workspace_layout", "fsa_bounds", "fsa_forward", "fsa_copy_eligibility",
     "fsa_attention", "fsa_attention_workspace_bytes", "fsa_cross_attention",
     "fsa_cross_attention_workspace_bytes", "fsa_prep_weight_bytes", "fsa_prep_pack_weights",
@@ -98,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.fsa_plan_valid_pairs.restype = c_int64
     L.fsa_plan_key_tokens.argtypes = [P]
     L.fsa_plan_key_tokens.restype = c_int64
+    L.fsa_plan_row_block.argtypes = [P]
+    L.fsa_plan_row_block.restype = c_int32
+    L.fsa_plan_set_row_block.argtypes = [P, c_int32]
+    L.fsa_plan_set_row_block.restype = c_int32
     L.fsa_workspace_bytes.argtypes = [P]
     L.fsa_workspace_bytes.restype = c_size_t
     L.fsa_workspace_layout.argtypes = [P, POINTER(fsa_ws_layout)]
@@ -246,6 +251,14 @@ def fsa_plan_key_tokens(plan: Plan) -> int:
     return int(lib().fsa_plan_key_tokens(plan))
 
 
+def fsa_plan_row_block(plan: Plan) -> int:
+    return int(lib().fsa_plan_row_block(plan))
+
+
+def fsa_plan_set_row_block(plan: Plan, rows: int) -> None:
+    _check(lib().fsa_plan_set_row_block(plan, int(rows)))
+
+
 def fsa_workspace_bytes(plan: Plan) -> int:
     return int(lib().fsa_workspace_bytes(plan))
 
@@ -340,6 +353,21 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
+def _check_out_ws(out, ws, like, need: int) -> None:
+    """The C ABI cannot see buffer sizes: reject an output or workspace that
+    the kernels would overrun or misread."""
+    if out is not None:
+        if not out.is_cuda or out.device != like.device or not out.is_contiguous() \
+                or tuple(out.shape) != tuple(like.shape) or out.dtype != like.dtype:
+            raise ValueError(f"out must be a contiguous CUDA tensor of shape {tuple(like.shape)} "
+                             f"and dtype {like.dtype} on {like.device}")
+    if ws is not None:
+        if not ws.is_cuda or ws.device != like.device or not ws.is_contiguous() \
+                or ws.numel() * ws.element_size() < need:
+            raise ValueError(f"ws must be a contiguous CUDA tensor of at least {need} bytes on "
+                             f"{like.device}")
+
+
 def attention(q, k, v, F: int, T: int, window: int, ref_frame: int, scale: float | None = None,
               mode="auto", out=None, ws=None):
     """O = frame-aligned windowed attention of [B, H, F*T, d] CUDA tensors.
@@ -358,6 +386,7 @@ def attention(q, k, v, F: int, T: int, window: int, ref_frame: int, scale: float
         scale = d ** -0.5
     code = dtype_code(q)
     need = fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, code)
+    _check_out_ws(out, ws, q, need)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
@@ -387,6 +416,7 @@ def cross_attention(q, kr, vr, F: int, T: int, scale: float | None = None, mode=
         scale = d ** -0.5
     code = dtype_code(q)
     need = fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, code)
+    _check_out_ws(out, ws, q, need)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:

@@ -189,6 +189,27 @@ int64_t fsa_plan_valid_pairs(const fsa_plan* plan);
    or M for a cross plan. -1 for a NULL plan. */
 int64_t fsa_plan_key_tokens(const fsa_plan* plan);
 
+/*
+ * fsa_plan_row_block -- query rows one workgroup of the bf16 forward kernel
+ * computes for this plan: consecutive rows of one frame, 256 (8 waves of 32
+ * rows, one workgroup per CU sharing each staged key chunk) or 128 (4 waves,
+ * two workgroups per CU). FSA_MODE_AUTO_ROWS decides the route per such
+ * block. 1 for an fp32 plan (one row per thread), -1 for a NULL plan. The
+ * geometry changes only how rows are grouped, never the result's arithmetic
+ * per row ("Unchaining the Softmax" ¶3: block shapes re-tuned with the
+ * softmax).
+ */
+int32_t fsa_plan_row_block(const fsa_plan* plan);
+
+/*
+ * fsa_plan_set_row_block -- replace the plan's own choice of row block
+ * (rows = 128 or 256; 0 restores the plan's choice; an fp32 plan accepts only
+ * 0 or 1). For measurement and tests. Not thread-safe against calls using the
+ * same plan; plans cached by fsa_attention are never changed.
+ * Errors: FSA_ERR_INVALID_ARG (NULL plan, another value).
+ */
+fsa_status fsa_plan_set_row_block(fsa_plan* plan, int32_t rows);
+
 /* Workspace size in bytes for this plan, and where each product lives. */
 size_t fsa_workspace_bytes(const fsa_plan* plan);
 fsa_status fsa_workspace_layout(const fsa_plan* plan, fsa_ws_layout* out);

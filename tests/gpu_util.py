@@ -30,7 +30,7 @@ def dtype_code(cfg: Config) -> int:
 class Run:
     """One bounds + forward pass of a config through the C ABI."""
 
-    def __init__(self, cfg: Config, seed=0, inputs=None, bq=0, bk=0):
+    def __init__(self, cfg: Config, seed=0, inputs=None, bq=0, bk=0, row_block=0):
         self.cfg = cfg
         if inputs is None:
             inputs = make_inputs(cfg, seed=seed, device="cuda")
@@ -43,6 +43,9 @@ class Run:
             shape = fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
                                    cfg.ref_frame, bq, bk, dtype_code(cfg))
             self.plan = fsa.fsa_plan_create(shape)
+        if row_block:
+            fsa.fsa_plan_set_row_block(self.plan, row_block)
+        self.row_block = fsa.fsa_plan_row_block(self.plan)
         self.ws = torch.zeros(fsa.fsa_workspace_bytes(self.plan), dtype=torch.uint8,
                               device="cuda")
         self.K_before = None

@@ -226,3 +226,44 @@ def test_prep_validates_before_launch():
         with pytest.raises(fsa.FsaError) as e:
             fn()
         assert e.value.status == status, fsa.fsa_last_error()
+
+
+def test_row_block_choice_and_override():
+    """The bf16 forward kernel's row block: the plan's own choice, both
+    geometries on request, and rejected values; fp32 plans compute a row per
+    thread."""
+    p = fsa.fsa_plan_create(shape(dtype=fsa.FSA_BF16, d=128, T=3600, F=13, H=24, window=2))
+    assert fsa.fsa_plan_row_block(p) == 128
+    fsa.fsa_plan_set_row_block(p, 256)
+    assert fsa.fsa_plan_row_block(p) == 256
+    fsa.fsa_plan_set_row_block(p, 0)
+    assert fsa.fsa_plan_row_block(p) == 128
+    for bad in (64, 192, 512, -1):
+        with pytest.raises(fsa.FsaError) as e:
+            fsa.fsa_plan_set_row_block(p, bad)
+        assert e.value.status == fsa.FSA_ERR_INVALID_ARG
+    # the tile list does not depend on the kernel's geometry
+    before = fsa.fsa_plan_export(p)
+    fsa.fsa_plan_set_row_block(p, 256)
+    after = fsa.fsa_plan_export(p)
+    assert all((before[k] == after[k]).all() for k in ("row_ptr", "col_idx", "qframe", "runs"))
+    q = fsa.fsa_plan_create(shape())                 # fp32
+    assert fsa.fsa_plan_row_block(q) == 1
+    fsa.fsa_plan_set_row_block(q, 0)
+    with pytest.raises(fsa.FsaError):
+        fsa.fsa_plan_set_row_block(q, 128)
+    assert fsa.lib().fsa_plan_row_block(None) == -1
+
+
+def test_attention_rejects_bad_out_and_workspace():
+    """fsa.attention / fsa.cross_attention check a caller-supplied output and
+    workspace before anything reaches the C ABI (which cannot see sizes)."""
+    import torch
+    q = torch.zeros(1, 2, 5 * 48, 64)        # CPU tensors: rejected before any launch
+    with pytest.raises(ValueError):
+        fsa._check_out_ws(torch.zeros(1, 2, 5 * 48, 32), None, q, 1024)   # wrong shape
+    with pytest.raises(ValueError):
+        fsa._check_out_ws(torch.zeros_like(q), None, q, 1024)              # not on a GPU
+    with pytest.raises(ValueError):
+        fsa._check_out_ws(None, torch.zeros(8, dtype=torch.uint8), q, 1024)   # not on a GPU
+    fsa._check_out_ws(None, None, q, 1024)                                 # nothing given

@@ -60,12 +60,14 @@ def test_cross_bounds_parity_small():
     assert np.array_equal(host[0], elig)
 
 
-def test_cross_small_full():
-    """Every mode on the whole small workload; the loose head takes the online
-    route bit-identically under AUTO and ONLINE_ONLY."""
+@pytest.mark.parametrize("row_block", (128, 256))
+def test_cross_small_full(row_block):
+    """Every mode on the whole small workload, in both workgroup geometries;
+    the loose head takes the online route bit-identically under AUTO and
+    ONLINE_ONLY."""
     cfg = CONFIGS["xref-small"]
-    say("cross forward", cfg.name)
-    run = Run(cfg).bounds()
+    say("cross forward", cfg.name, row_block)
+    run = Run(cfg, row_block=row_block).bounds()
     Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
     want = orc.cross_attention(Q, K, V, cfg.scale)
     outs = {}
@@ -103,8 +105,9 @@ def test_cross_720p_sampled():
         print(f"720p-xref h{h}: max {mx:.3g} mean {mean:.3g}")
 
 
+@pytest.mark.parametrize("row_block", (128, 256))
 @pytest.mark.parametrize("M", [16, 48, 720, 3600])
-def test_cross_probe_granule_counts(M):
+def test_cross_probe_granule_counts(M, row_block):
     """Q = 0 and V_j = one-hot((j // 16) mod d): every row's output is the
     share of each granule class among the M reference keys, known exactly,
     so a dropped or doubled 16-key granule shows up far above bf16 rounding
@@ -118,7 +121,7 @@ def test_cross_probe_granule_counts(M):
     V = torch.zeros((1, 1, M, cfg.d), device="cuda", dtype=torch.bfloat16)
     idx = torch.arange(M, device="cuda")
     V[0, 0, idx, (idx // 16) % cfg.d] = 1
-    run = Run(cfg, inputs=(Q, K, V)).bounds()
+    run = Run(cfg, inputs=(Q, K, V), row_block=row_block).bounds()
     O = run.forward()[0, 0].double().cpu().numpy()
     want = np.bincount((np.arange(M) // 16) % cfg.d, minlength=cfg.d) / M
     assert np.max(np.abs(O - want[None, :])) <= 4e-3 * want.max()

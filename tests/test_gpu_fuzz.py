@@ -7,7 +7,7 @@ against the oracle (bf16: max-abs 2e-2, mean-abs 2e-3; fp32: max-abs 1e-5)
 and the two launches bit for bit. Cross-attention cases draw a reference-set
 size instead of a window. The shapes cover single frames, frames shorter than
 one workgroup, spans that leave ragged row units and key chunks, and both
-kernels' head widths.
+kernels' head widths, in both workgroup geometries of the bf16 kernel.
 """
 import os
 
@@ -41,7 +41,10 @@ def draw_case(i: int):
         ref_frame=0 if cross else int(rng.integers(0, F)),
         M=16 * int(rng.integers(1, 81)) if cross else 0,
         key_sigma=float(rng.choice([1.0, 2.0])))
-    return cfg, str(rng.choice(MODES))
+    mode = str(rng.choice(MODES))
+    # bf16: the forward kernel's workgroup geometry (128 or 256 rows)
+    row_block = int(rng.choice([128, 256])) if dtype == "bf16" else 0
+    return cfg, mode, row_block
 
 
 # FSA_FUZZ_CASES widens the sweep for a one-off run (the default keeps the
@@ -51,9 +54,9 @@ N_CASES = int(os.environ.get("FSA_FUZZ_CASES", "24"))
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape(i):
-    cfg, mode = draw_case(i)
-    say("fuzz", i, cfg, mode)
-    run = Run(cfg, seed=i).bounds()
+    cfg, mode, row_block = draw_case(i)
+    say("fuzz", i, cfg, mode, row_block)
+    run = Run(cfg, seed=i, row_block=row_block).bounds()
     O1 = run.forward(mode)
     O2 = run.forward(mode)
     assert torch.equal(O1, O2), "two launches differ"

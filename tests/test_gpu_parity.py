@@ -19,6 +19,10 @@ from gpu_util import (BF16_MAX_ABS, Run, assert_close, errors, oracle_rows, samp
 
 pytestmark = pytest.mark.gpu
 
+# Workgroup geometries of the bf16 forward kernel: the plan's own choice (128
+# rows, 4 waves, for every bf16 shape here) and the 8-wave 256-row one.
+ROW_BLOCKS = (128, 256)
+
 if not torch.cuda.is_available():   # collected on CPU too; every test here is gpu-marked
     pytest.skip("no GPU", allow_module_level=True)
 
@@ -94,10 +98,11 @@ def test_tiny_fp32_full():
         assert_close(cfg, O, want, f"tiny {mode}")
 
 
-def test_small_bf16_full():
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
+def test_small_bf16_full(row_block):
     cfg = CONFIGS["small"]
-    say("forward small bf16")
-    run = Run(cfg).bounds()
+    say("forward small bf16", row_block)
+    run = Run(cfg, row_block=row_block).bounds()
     O = run.forward("auto")
     Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
     want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
@@ -109,12 +114,15 @@ def test_small_bf16_full():
 
 # ------------------------------------------------------------------ forward, full size sampled
 
-@pytest.mark.parametrize("name,heads", [("720p", [0, 11, 23]), ("1080p", [0, 17]),
-                                        ("stress", [6, 7, 33]), ("720p-dense", [0, 13])])
-def test_full_size_sampled(name, heads):
+@pytest.mark.parametrize("name,heads,row_block", [
+    ("720p", [0, 11, 23], 0), ("1080p", [0, 17], 0), ("stress", [6, 7, 33], 0),
+    ("720p-dense", [0, 13], 0), ("720p", [0, 23], 256), ("stress", [7, 33], 256)])
+def test_full_size_sampled(name, heads, row_block):
+    """Sampled rows at full size: in the plan's own launch configuration (the
+    one the benchmark times) and in the 8-wave one."""
     cfg = CONFIGS[name]
-    say("forward full size", name)
-    run = Run(cfg).bounds()
+    say("forward full size", name, row_block)
+    run = Run(cfg, row_block=row_block).bounds()
     O = run.forward("auto")
     assert bool(torch.isfinite(O).all())
     for h in heads:
@@ -237,12 +245,13 @@ def probe_inputs(cfg, q_zero, v_kind, seed=0):
     return Q, K, V
 
 
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
 @pytest.mark.parametrize("name", ["small", "720p"])
-def test_probe_frame_one_hot(name):
+def test_probe_frame_one_hot(name, row_block):
     """V_j = one-hot(frame of j): weight outside the slice is exactly zero."""
     cfg = CONFIGS[name].with_(H=2)
-    say("probe frame", name)
-    run = Run(cfg, inputs=probe_inputs(cfg, False, "frame")).bounds()
+    say("probe frame", name, row_block)
+    run = Run(cfg, inputs=probe_inputs(cfg, False, "frame"), row_block=row_block).bounds()
     O = run.forward()[0].float().cpu().numpy()
     frame = np.arange(cfg.N) // cfg.T
     for f in range(cfg.F):
@@ -253,14 +262,18 @@ def test_probe_frame_one_hot(name):
         assert np.all(np.abs(blk[:, :, :cfg.F].sum(-1) - 1.0) < 2e-2), f
 
 
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
 @pytest.mark.parametrize("name", ["tiny", "small", "720p", "1080p"])
-def test_probe_granule_counts(name):
+def test_probe_granule_counts(name, row_block):
     """Q = 0 and V_j = one-hot((j // 16) mod d): every row's output is the
     share of its slice's 16-key granules in each class, known exactly, so a
     dropped or doubled granule shows up far above bf16 rounding."""
     cfg = CONFIGS[name].with_(H=1)
-    say("probe granules", name)
-    run = Run(cfg, inputs=probe_inputs(cfg, True, "granule")).bounds()
+    if cfg.dtype != "bf16" and row_block != ROW_BLOCKS[0]:
+        pytest.skip("an fp32 plan has one geometry (a row per thread)")
+    say("probe granules", name, row_block)
+    run = Run(cfg, inputs=probe_inputs(cfg, True, "granule"),
+              row_block=row_block if cfg.dtype == "bf16" else 0).bounds()
     O = run.forward()[0, 0].double().cpu().numpy()
     for f in range(cfg.F):
         keys = orc.slice_keys(cfg.F, cfg.T, cfg.window, cfg.ref_frame, f)
@@ -288,13 +301,16 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
-def test_edge_shapes(case):
+def test_edge_shapes(case, row_block):
     name, F, T, H, d, dt, w, r = case
+    if dt != "bf16" and row_block != ROW_BLOCKS[0]:
+        pytest.skip("an fp32 plan has one geometry (a row per thread)")
     cfg = CONFIGS["small"].with_(name=name, F=F, T=T, H=H, d=d, dtype=dt, window=w,
                                  ref_frame=r, B=2 if name == "batch-2" else 1)
-    say("edge", case)
-    run = Run(cfg).bounds()
+    say("edge", case, row_block)
+    run = Run(cfg, row_block=row_block if dt == "bf16" else 0).bounds()
     O = run.forward()
     Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
     want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
@@ -330,14 +346,15 @@ def test_attention_entry_point():
 
 
 def test_split_workgroups_exact_and_deterministic():
-    """T = 3600 leaves each frame's last workgroup a single row unit, which
-    its four waves split over the key chunks and then combine through LDS.
+    """In 4-wave workgroups (128 rows), T = 3600 leaves each frame's last
+    workgroup a single row unit, which its four waves split over the key
+    chunks and then combine through LDS.
     Every row of those units, in every frame and head, on both routes, against
     the oracle; and three launches of each route bit-identical (a combine that
     read partials before they landed would show in both)."""
     cfg = CONFIGS["720p"].with_(F=5, H=4)
     say("split workgroups", cfg.name)
-    run = Run(cfg).bounds()
+    run = Run(cfg, row_block=128).bounds()
     rows = np.concatenate([np.arange(f * cfg.T + 3584, (f + 1) * cfg.T) for f in range(cfg.F)])
     for mode in ("auto", "online"):
         outs = [run.forward(mode) for _ in range(3)]
