@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <tuple>
 
@@ -151,12 +152,15 @@ namespace {
 using Key = std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
                        int32_t>;
 
+// Cached plans are shared: a call holds its own reference while it uses the
+// plan, so fsa_cache_clear on another thread only drops the cache's.
+using PlanRef = std::shared_ptr<const fsa_plan>;
 std::mutex g_cache_mu;
-std::map<Key, fsa_plan*> g_cache;
+std::map<Key, PlanRef> g_cache;
 
 // Looks up or builds the plan of a shape (bq = bk = 0; M > 0: a cross plan).
 // Caller holds no lock.
-fsa_status cached_plan(const fsa_shape& s, int32_t M, const fsa_plan** out) {
+fsa_status cached_plan(const fsa_shape& s, int32_t M, PlanRef* out) {
     const Key key{s.B, s.H, s.F, s.T, s.d, s.window, s.ref_frame, s.dtype, M};
     std::lock_guard<std::mutex> lock(g_cache_mu);
     auto it = g_cache.find(key);
@@ -168,13 +172,13 @@ fsa_status cached_plan(const fsa_shape& s, int32_t M, const fsa_plan** out) {
     fsa_status st = M > 0 ? fsa_plan_create_cross(&s, M, &p) : fsa_plan_create(&s, &p);
     if (st != FSA_OK) return st;
     try {
-        g_cache.emplace(key, p);
+        PlanRef ref(p, [](const fsa_plan* q) { fsa_plan_destroy(const_cast<fsa_plan*>(q)); });
+        g_cache.emplace(key, ref);
+        *out = std::move(ref);
     } catch (...) {
-        fsa_plan_destroy(p);
         set_error("fsa_attention: out of host memory");
         return FSA_ERR_NOMEM;
     }
-    *out = p;
     return FSA_OK;
 }
 
@@ -190,14 +194,13 @@ fsa_shape make_shape(int32_t F, int32_t T, int32_t window, int32_t ref_frame, in
 
 extern "C" void fsa_cache_clear(void) {
     std::lock_guard<std::mutex> lock(g_cache_mu);
-    for (auto& kv : g_cache) fsa_plan_destroy(kv.second);
-    g_cache.clear();
+    g_cache.clear();     // plans still in use by a call are freed when it ends
 }
 
 extern "C" size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t window,
                                                 int32_t ref_frame, int32_t B, int32_t H,
                                                 int32_t d, int32_t dtype) {
-    const fsa_plan* p = nullptr;
+    PlanRef p;
     if (cached_plan(make_shape(F, T, window, ref_frame, B, H, d, dtype), 0, &p) != FSA_OK)
         return 0;
     return p->ws.total;
@@ -222,9 +225,10 @@ fsa_status attend(const char* who, const void* Q, const void* K, const void* V, 
         set_error("%s: unknown mode %d", who, mode);
         return FSA_ERR_INVALID_ARG;
     }
-    const fsa_plan* p = nullptr;
-    fsa_status st = cached_plan(shape, M, &p);
+    PlanRef ref;
+    fsa_status st = cached_plan(shape, M, &ref);
     if (st != FSA_OK) return st;
+    const fsa_plan* p = ref.get();
     if (!ws || ws_bytes < p->ws.total) {
         set_error("%s: workspace of %zu bytes, %zu needed", who, ws ? ws_bytes : size_t(0),
                   p->ws.total);
@@ -266,7 +270,7 @@ extern "C" fsa_status fsa_attention(const void* Q, const void* K, const void* V,
 
 extern "C" size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int32_t B,
                                                       int32_t H, int32_t d, int32_t dtype) {
-    const fsa_plan* p = nullptr;
+    PlanRef p;
     if (M <= 0) {
         set_error("fsa_cross_attention_workspace_bytes: M=%d must be positive", M);
         return 0;

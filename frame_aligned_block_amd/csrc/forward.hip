@@ -127,9 +127,10 @@ __device__ __forceinline__ bool row_gap_ok(float g, float c) {
 }
 
 // Whether the (batch*head, frame) pairs of this launch take different routes
-// (then their costs differ by the online route's ~1.3x). Every workgroup reads
-// the same flags and reaches the same answer; launches past kMixScan pairs
-// are treated as uniform.
+// (then their costs differ by the online route's ~1.3x). Every wave reads all
+// the flags itself (no LDS, no barrier) and every wave of every workgroup
+// reaches the same answer; launches past kMixScan pairs are treated as
+// uniform.
 constexpr int kMixScan = 4096;
 
 __device__ __forceinline__ bool routes_mixed(const FwdArgs& p) {
@@ -147,9 +148,9 @@ __device__ __forceinline__ bool routes_mixed(const FwdArgs& p) {
     }
     if (n > kMixScan) return false;
     const uint8_t first = fl[0];
-    int diff = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) diff |= fl[i] != first;
-    return __syncthreads_or(diff) != 0;
+    bool diff = false;
+    for (int i = threadIdx.x & 63; i < n; i += 64) diff |= fl[i] != first;
+    return __builtin_amdgcn_ballot_w64(diff) != 0;
 }
 
 // The pair of the ti-th place in the launch order. Uniform launches walk the
@@ -250,13 +251,20 @@ __device__ __forceinline__ void issue_chunk4(unsigned stage_lds, const Slice& sl
             issue_group<D, 4>(stage_lds, sl, Kh, Vh, ch, wave + 2 * r, lane, i);
 }
 
-// 8-wave workgroups: every wave issues its own groups of the chunk.
+// 8-wave workgroups: waves 0-3 (one per SIMD) issue the whole chunk, wave w
+// also the groups of wave w + 4. Right after a barrier the copying waves stall
+// while the CU's address path takes their copies and waves 4-7 run ahead,
+// which puts the two waves of each SIMD out of phase again (the barrier had
+// lined them up): measured 2.6-3.6% faster than all 8 waves copying.
 template <int D>
 __device__ __forceinline__ void issue_chunk8(unsigned stage_lds, const Slice& sl, const __bf16* Kh,
                                              const __bf16* Vh, int ch, int wave, int lane) {
+    if (wave >= 4) return;
 #pragma unroll
-    for (int i = 0; i < Geo<D>::BLOCKS / 8; ++i)
-        issue_group<D, 8>(stage_lds, sl, Kh, Vh, ch, wave, lane, i);
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < Geo<D>::BLOCKS / 8; ++i)
+            issue_group<D, 8>(stage_lds, sl, Kh, Vh, ch, wave + 4 * r, lane, i);
 }
 
 // Per-lane LDS byte offsets (constant for the whole walk).
@@ -640,11 +648,12 @@ template <int D>
 __device__ __forceinline__ void walk8_prologue(unsigned lds0, const Slice& sl, const __bf16* Kh,
                                                const __bf16* Vh, int nchunks, int wave, int lane) {
     using GG = Geo<D>;
-    constexpr int CPW = 2 * (GG::BLOCKS / 8);          // copies per wave per chunk
+    constexpr int CPW = 2 * (GG::BLOCKS / 4);          // copies per copying wave per chunk
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch)
         if (ch < nchunks) issue_chunk8<D>(lds0 + ch * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
-    // chunks 0 and 1 have landed; 2 and 3 may still be in flight
+    // chunks 0 and 1 have landed; 2 and 3 may still be in flight (waves 4-7
+    // have issued nothing, so every wait passes at once for them)
     if (nchunks >= 4) FSA_WAIT_VMCNT(2 * CPW);
     else if (nchunks == 3) FSA_WAIT_VMCNT(CPW);
     else FSA_WAIT_VMCNT(0);
@@ -777,17 +786,55 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
     FSA_WAIT_VMCNT(0);
 }
 
+// The 8-wave counterpart of attend_split: a workgroup left with a single row
+// unit (T = 3600 leaves one 16-row granule after 14 full 256-row workgroups).
+// Every wave takes that unit; wave w computes on the w-th 16-key granule of
+// every pair of chunks (chunk 2p + w / 4, granule w % 4), all waves passing
+// the barriers of the ring as in attend8. combine_split adds the partials up.
+template <int D, int G, bool FIXED>
+__device__ __forceinline__ void attend_split8(unsigned char* smem, const Slice& sl,
+                                              const __bf16* Kh, const __bf16* Vh,
+                                              const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
+                                              float c, f32x4 (&o)[G][D / 16], float (&rs)[G],
+                                              float (&m)[G], int wave, int lane) {
+    using GG = Geo<D>;
+    const LaneAddr la = lane_addr(lane & 15, lane >> 4);
+    const int nchunks = (sl.total + kBK - 1) / kBK;
+    const int nsteps = (sl.total + 31) >> 5;
+    const int npairs = (nchunks + 1) >> 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = -INFINITY;
+    const unsigned lds0 = unsigned(uintptr_t((lds_void*)smem));
+    walk8_prologue<D>(lds0, sl, Kh, Vh, nchunks, wave, lane);
+    for (int p = 0; p < npairs; ++p) {
+        const int ch = 2 * p + (wave >> 2), k0 = 16 * (wave & 3);
+        if (ch * kBK + k0 < sl.total) {                         // this wave's granule exists
+            const unsigned char* S0 = smem + (ch & 3) * GG::STAGE;
+            f32x4 sv[2][G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            scores<D, G, 1>(S0, k0, qf, sv, la);
+            bf16x2 pk[G][2];
+            softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+            pv_half<D, G>(S0 + GG::TILE, k0, pk, o, la);
+        }
+        // the barrier of pair p sits in step 4p + 3, as in attend8
+        if (4 * p + 3 + 1 < nsteps) walk8_barrier<D>(lds0, sl, Kh, Vh, p, nchunks, wave, lane);
+    }
+    FSA_WAIT_VMCNT(0);
+}
+
 // Floats per lane that a wave of a split workgroup hands over: its partial
 // output accumulators, row sums and running maxima.
 template <int D, int G>
 constexpr int split_floats() { return G * (D / 16) * 4 + 2 * G; }
 
-// Adds the partial results of a split (4-wave) workgroup's waves into wave 0, in
+// Adds the partial results of a split workgroup's W waves into wave 0, in
 // wave order (so the sum is deterministic), through the LDS the key ring used.
 // The fixed route's partial sums share one shift and simply add; the online
 // route rescales each to the largest running max first. Returns true in wave
 // 0 only, which then holds the whole row sums and accumulators.
-template <int D, int G>
+template <int D, int G, int W>
 __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G][D / 16],
                                               float (&rs)[G], float (&m)[G], float c, bool fixed,
                                               int wave, int lane) {
@@ -815,7 +862,7 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
     FSA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
     if (wave > 0) return false;
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < W; ++w) {
         const float* theirs = buf + (w - 1) * NF * 64 + lane;
         constexpr int RS = G * (D / 16) * 4, MX = RS + G;
         if (fixed) {
@@ -849,12 +896,12 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
 }
 
 // LDS of a workgroup: the key ring (4 stages for 8 waves, 2 for 4 waves); a
-// split 4-wave workgroup reuses it to combine its waves' partials.
+// split workgroup reuses it to combine its waves' partials.
 template <int D, int G, int W>
 constexpr int fwd_lds_bytes() {
-    return W == 8 ? 4 * Geo<D>::STAGE
-                  : (2 * Geo<D>::STAGE > 3 * split_floats<D, G>() * 64 * 4
-                         ? 2 * Geo<D>::STAGE : 3 * split_floats<D, G>() * 64 * 4);
+    constexpr int ring = (W == 8 ? 4 : 2) * Geo<D>::STAGE;
+    constexpr int partials = (W - 1) * split_floats<D, G>() * 64 * 4;
+    return ring > partials ? ring : partials;
 }
 
 // W waves of 16*G rows each; two waves per SIMD (<= 256 registers per lane):
@@ -888,11 +935,11 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
     // frame (the tail of a frame whose granule count G does not divide)
     // repeat the frame's last granule and are not stored: every computing
     // wave runs the same loop, with no predicate inside it. A wave wholly
-    // past the last unit only helps stage the keys, except in a 4-wave
-    // workgroup left with a single unit: there every wave takes that unit and
-    // a share of the key chunks (attend_split).
+    // past the last unit only helps stage the keys, except in a workgroup
+    // left with a single unit: there every wave takes that unit and a share
+    // of the key chunks (attend_split, attend_split8).
     const int first_unit = gq * W;
-    const bool split = W == 4 && p.units_per_frame - first_unit == 1;   // uniform
+    const bool split = p.units_per_frame - first_unit == 1;   // uniform
     const int unit = split ? first_unit : first_unit + wave;
     const int ngran = T >> 4;
     const int nvalid = max(0, min(G, ngran - unit * G));     // uniform per wave
@@ -975,16 +1022,23 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
 #pragma unroll
     for (int g = 0; g < G; ++g) shift[g] *= c;
 
-    if (W == 8) {
+    if (split) {
+        float m[G];
+        if (W == 8) {
+            if (fixed)
+                attend_split8<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+            else
+                attend_split8<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        } else {
+            if (fixed)
+                attend_split<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+            else
+                attend_split<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        }
+        if (!combine_split<D, G, W>(smem, o, rs, m, c, fixed, uwave, lane)) return;
+    } else if (W == 8) {
         if (fixed) attend8<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
         else attend8<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
-    } else if (split) {
-        float m[G];
-        if (fixed)
-            attend_split<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-        else
-            attend_split<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-        if (!combine_split<D, G>(smem, o, rs, m, c, fixed, uwave, lane)) return;
     } else if (fixed) {
         attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
     } else {

@@ -19,7 +19,9 @@ from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_voi
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfsa.so")
+# FSA_LIBRARY names another build of the same library (the sanitizer build of
+# the host code the CPU tests load); the default is the in-tree libfsa.so.
+LIB_PATH = os.environ.get("FSA_LIBRARY") or os.path.join(_HERE, "libfsa.so")
 
 FSA_OK = 0
 FSA_ERR_INVALID_ARG = -1

@@ -306,7 +306,9 @@ fsa_status fsa_cross_attention(const void* Q, const void* Kr, const void* Vr, vo
 size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int32_t B, int32_t H,
                                            int32_t d, int32_t dtype);
 
-/* Drop every cached plan of fsa_attention and fsa_cross_attention. */
+/* Drop every cached plan of fsa_attention and fsa_cross_attention. Safe to
+   call while other threads are inside those calls: a call keeps the plan it
+   looked up until it returns. */
 void fsa_cache_clear(void);
 
 /*

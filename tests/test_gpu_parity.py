@@ -345,16 +345,17 @@ def test_attention_entry_point():
     assert torch.equal(run.forward(), O)
 
 
-def test_split_workgroups_exact_and_deterministic():
-    """In 4-wave workgroups (128 rows), T = 3600 leaves each frame's last
-    workgroup a single row unit, which its four waves split over the key
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
+def test_split_workgroups_exact_and_deterministic(row_block):
+    """T = 3600 leaves each frame's last workgroup a single row unit (in
+    128-row and in 256-row workgroups), which its waves split over the key
     chunks and then combine through LDS.
     Every row of those units, in every frame and head, on both routes, against
     the oracle; and three launches of each route bit-identical (a combine that
     read partials before they landed would show in both)."""
     cfg = CONFIGS["720p"].with_(F=5, H=4)
-    say("split workgroups", cfg.name)
-    run = Run(cfg, row_block=128).bounds()
+    say("split workgroups", cfg.name, row_block)
+    run = Run(cfg, row_block=row_block).bounds()
     rows = np.concatenate([np.arange(f * cfg.T + 3584, (f + 1) * cfg.T) for f in range(cfg.F)])
     for mode in ("auto", "online"):
         outs = [run.forward(mode) for _ in range(3)]
