@@ -103,10 +103,15 @@ extern "C" fsa_status fsa_forward(const fsa_plan* plan, const void* Q, const voi
         set_error("fsa_forward: scale must be finite and > 0 (got %g)", double(scale));
         return FSA_ERR_INVALID_ARG;
     }
-    if (mode != FSA_MODE_AUTO && mode != FSA_MODE_ONLINE_ONLY && mode != FSA_MODE_FIXED_ONLY &&
-        mode != FSA_MODE_AUTO_FRAME && mode != FSA_MODE_AUTO_ROWS) {
+    const int32_t route = mode & ~FSA_MODE_RECORD_PMAX;
+    if (route != FSA_MODE_AUTO && route != FSA_MODE_ONLINE_ONLY && route != FSA_MODE_FIXED_ONLY &&
+        route != FSA_MODE_AUTO_FRAME && route != FSA_MODE_AUTO_ROWS) {
         set_error("fsa_forward: unknown mode %d", mode);
         return FSA_ERR_INVALID_ARG;
+    }
+    if ((mode & FSA_MODE_RECORD_PMAX) && plan->shape.dtype != FSA_BF16) {
+        set_error("fsa_forward: FSA_MODE_RECORD_PMAX needs a bf16 plan");
+        return FSA_ERR_UNSUPPORTED;
     }
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16)) {
         set_error("fsa_forward: Q, K, V and O must be 16-byte aligned");

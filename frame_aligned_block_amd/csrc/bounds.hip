@@ -242,12 +242,14 @@ __global__ __launch_bounds__(256) void bounds_radius(
 __global__ __launch_bounds__(256) void bounds_finalize(
     const float* __restrict__ partqmax, const float* __restrict__ partmax,
     float* __restrict__ rframe, float* __restrict__ rslice, float* __restrict__ stat,
-    uint8_t* __restrict__ elig, float* __restrict__ statf, uint8_t* __restrict__ eligf, int F,
-    int KF, PartsArg qp, PartsArg kp, float scale, const FrameTable tab) {
+    uint8_t* __restrict__ elig, float* __restrict__ statf, uint8_t* __restrict__ eligf,
+    unsigned* __restrict__ pmax, int F, int KF, PartsArg qp, PartsArg kp, float scale,
+    const FrameTable tab) {
     __shared__ float rf[FSA_MAX_FRAMES + 1];
     __shared__ float qm[FSA_MAX_FRAMES + 1];
     __shared__ float sb[FSA_MAX_FRAMES + 1];
     const int bh = blockIdx.x;
+    if (bh == 0 && threadIdx.x == 0) *pmax = 0u;      // forward's probability record starts over
     for (int g = threadIdx.x; g < KF; g += blockDim.x) {
         float b = 0.f;
         for (int s = 0; s < kp.per_frame; ++s)
@@ -365,7 +367,8 @@ fsa_status launch_bounds_finalize(const fsa_plan& p, char* ws, float scale, hipS
                        reinterpret_cast<float*>(ws + p.ws.stat),
                        reinterpret_cast<uint8_t*>(ws + p.ws.elig),
                        reinterpret_cast<float*>(ws + p.ws.statf),
-                       reinterpret_cast<uint8_t*>(ws + p.ws.eligf), s.F, p.key_frames, qp, kp,
+                       reinterpret_cast<uint8_t*>(ws + p.ws.eligf),
+                       reinterpret_cast<unsigned*>(ws + p.ws.pmax), s.F, p.key_frames, qp, kp,
                        scale, p.table);
     hipLaunchKernelGGL(bounds_slice_mean, dim3(s.F, s.B * s.H), dim3(128), 0, stream,
                        reinterpret_cast<const float*>(ws + p.bounds.colsum),

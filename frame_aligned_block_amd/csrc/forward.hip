@@ -71,6 +71,7 @@ struct FwdArgs {
     const uint8_t* elig;        // per (batch, head)
     const uint8_t* eligf;       // per (batch, head, frame)
     const float* dslice;        // slice mean key minus mu, per (batch, head, frame)
+    unsigned* pmax;             // largest fixed-route probability (float bits), kernels with PMAX
     float c;                    // scale * log2(e)
     int32_t N, T, F, BH;
     int32_t NK;                 // key (and value) tokens per (batch, head)
@@ -330,22 +331,33 @@ __device__ __forceinline__ float sum_pairs(const bf16x2* pp, int n, float acc) {
     return acc;
 }
 
+// Routes of the slice walks (template parameter R).
+constexpr int kOnline = 0;      // running reference max
+constexpr int kFixed = 1;       // shift fixed at the row's Cauchy-Schwarz bound
+constexpr int kFixedPmax = 2;   // kFixed, also keeping each row's largest p in m
+
 // Probabilities of NK scores of one granule-row. Fixed route: the shift is
-// the row's Cauchy-Schwarz bound. Online route: a running reference max,
+// the row's Cauchy-Schwarz bound; kFixedPmax keeps the largest probability
+// formed (before rounding to bf16) in m, which the fixed route does not use
+// otherwise. Online route: a running reference max,
 // moved (with the accumulator and row sum rescaled) only when a step's max
 // exceeds it by more than kLazyLog2 in log2 units, and only in the steps
 // where some row of the wave needs it; until then the row's probabilities
 // may reach 2^kLazyLog2, which bf16 and the fp32 sums hold as precisely.
 constexpr float kLazyLog2 = 8.f;
 
-template <int D, int G, bool FIXED, int NK>
+template <int D, int G, int R, int NK>
 __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const float (&shift)[G],
                                       float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
                                       float (&p)[NK]) {
-    if (FIXED) {
+    if (R != kOnline) {
 #pragma unroll
         for (int i = 0; i < NK; ++i)
             p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -shift[g]));
+        if (R == kFixedPmax) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i) m[g] = fmaxf(m[g], p[i]);
+        }
     } else {
         float mx = sv[0][0];
 #pragma unroll
@@ -383,7 +395,7 @@ __device__ __forceinline__ void load_v(const unsigned char* Vs, int koff, bf16x8
 // Softmax of one 32-key step (NB = 2) or of the lone 16-key granule (NB = 1)
 // into packed bf16 probabilities, the B operand of O^T += V^T P^T. The row
 // sum adds the bf16-rounded probabilities, the values the product consumes.
-template <int D, int G, bool FIXED, int NB>
+template <int D, int G, int R, int NB>
 __device__ __forceinline__ void softmax(const f32x4 (&s)[2][G], float c, const float (&shift)[G],
                                         float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
                                         bf16x2 (&pk)[G][2 * NB]) {
@@ -391,7 +403,7 @@ __device__ __forceinline__ void softmax(const f32x4 (&s)[2][G], float c, const f
     for (int g = 0; g < G; ++g) {
         const f32x4 sv[2] = {s[0][g], s[1][g]};
         float p[4 * NB];
-        probs<D, G, FIXED, 4 * NB>(sv, g, c, shift, m, rs, o, p);
+        probs<D, G, R, 4 * NB>(sv, g, c, shift, m, rs, o, p);
 #pragma unroll
         for (int i = 0; i < 2 * NB; ++i) pk[g][i] = bf16x2{__bf16(p[2 * i]), __bf16(p[2 * i + 1])};
         rs[g] = sum_pairs(pk[g], 2 * NB, rs[g]);
@@ -501,16 +513,15 @@ __device__ __forceinline__ void prio_vector_end() { __builtin_amdgcn_s_setprio(0
 // last holds 16 to kBK keys, whole 16-key granules. Scores are always
 // computed for 32 keys: past the slice end a stage holds copies of the
 // slice's last key (finite values) whose scores are never used.
-template <int D, int G, bool FIXED>
+template <int D, int G, int R>
 __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
                                        const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
-                                       float (&rs)[G], int wave, int lane) {
+                                       float (&rs)[G], float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     constexpr int SPC = kBK / 32;                       // 32-key steps per chunk
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
     const int nchunks = (sl.total + kBK - 1) / kBK;
-    float m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
 
@@ -536,17 +547,17 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
                 FSA_WAIT_VMCNT(0);                      // chunk ch+1 has landed
                 FSA_WAIT_LGKM0();                       // this step's V is in registers
                 __builtin_amdgcn_s_barrier();
-                if (FIXED && ch + 2 < nchunks)
+                if (R != kOnline && ch + 2 < nchunks)
                     issue_chunk4<D>(smem_lds + st * GG::STAGE, sl, Kh, Vh, ch + 2, wave, lane);
                 st ^= 1;
                 load_k<D>(smem + st * GG::STAGE, 0, ka, la);
             }
             bf16x2 pk[G][4];
             prio_vector_begin();
-            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
             prio_vector_end();
             __builtin_amdgcn_sched_barrier(0);
-            if (!FIXED && s + 1 == SPC) {
+            if (R == kOnline && s + 1 == SPC) {
                 // Online route: the copies of the chunk after next are issued
                 // between the k-steps of the matrix phase, which measured faster
                 // for it than issuing them right after the barrier (the fixed
@@ -576,16 +587,16 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
         if (k0 + 32 < left) {
             bf16x8 ka[GG::KS][2];
             load_k<D>(S0, k0 + 32, ka, la);
-            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
             qk_pv<D, G>(ka, qf, sv, va, pk, o);
         } else {
-            softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+            softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
             pv<D, G>(va, pk, o);
         }
     }
     if (left & 16) {                                    // the lone granule at k0
         bf16x2 pk[G][2];
-        softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+        softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
         pv_half<D, G>(S0 + GG::TILE, k0, pk, o, la);
     }
     FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
@@ -676,16 +687,15 @@ __device__ __forceinline__ void walk8_barrier(unsigned lds0, const Slice& sl, co
         if (ch < nchunks) issue_chunk8<D>(lds0 + (ch & 3) * GG::STAGE, sl, Kh, Vh, ch, wave, lane);
 }
 
-template <int D, int G, bool FIXED>
+template <int D, int G, int R>
 __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                         const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
                                         const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
-                                        float (&rs)[G], int wave, int lane) {
+                                        float (&rs)[G], float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
     const int nchunks = (sl.total + kBK - 1) / kBK;
     const int nsteps = (sl.total + 31) >> 5;
-    float m[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = -INFINITY;
     const unsigned lds0 = unsigned(uintptr_t((lds_void*)smem));
@@ -703,7 +713,7 @@ __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, co
         load_k<D>(smem + ((t1 >> 1) & 3) * GG::STAGE, 32 * (t1 & 1), ka, la);
         bf16x2 pk[G][4];
         prio_vector_begin();
-        softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+        softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
         prio_vector_end();
         __builtin_amdgcn_sched_barrier(0);
         qk_pv<D, G>(ka, qf, sv, va, pk, o);
@@ -716,11 +726,11 @@ __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, co
         bf16x8 va[GG::DB];
         load_v<D>(S0 + GG::TILE, 32 * (t & 1), va, la);
         bf16x2 pk[G][4];
-        softmax<D, G, FIXED, 2>(sv, c, shift, m, rs, o, pk);
+        softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
         pv<D, G>(va, pk, o);
     } else {
         bf16x2 pk[G][2];
-        softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+        softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
         pv_half<D, G>(S0 + GG::TILE, 32 * (t & 1), pk, o, la);
     }
     FSA_WAIT_VMCNT(0);                                  // no copy may outlive the workgroup
@@ -746,7 +756,7 @@ __device__ __forceinline__ void copy_only8(unsigned char* smem, const Slice& sl,
 // all waves staging and passing the barriers as usual. Each wave ends with
 // partial sums over its granules (and, on the online route, its running
 // max), which combine_split adds up.
-template <int D, int G, bool FIXED>
+template <int D, int G, int R>
 __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& sl,
                                              const __bf16* Kh, const __bf16* Vh,
                                              const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
@@ -771,7 +781,7 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
             for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
             scores<D, G, 1>(S0, 16 * wave, qf, sv, la);
             bf16x2 pk[G][2];
-            softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+            softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
             pv_half<D, G>(S0 + GG::TILE, 16 * wave, pk, o, la);
         }
         if (ch + 1 < nchunks) {
@@ -791,7 +801,7 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
 // Every wave takes that unit; wave w computes on the w-th 16-key granule of
 // every pair of chunks (chunk 2p + w / 4, granule w % 4), all waves passing
 // the barriers of the ring as in attend8. combine_split adds the partials up.
-template <int D, int G, bool FIXED>
+template <int D, int G, int R>
 __device__ __forceinline__ void attend_split8(unsigned char* smem, const Slice& sl,
                                               const __bf16* Kh, const __bf16* Vh,
                                               const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
@@ -815,7 +825,7 @@ __device__ __forceinline__ void attend_split8(unsigned char* smem, const Slice& 
             for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
             scores<D, G, 1>(S0, k0, qf, sv, la);
             bf16x2 pk[G][2];
-            softmax<D, G, FIXED, 1>(sv, c, shift, m, rs, o, pk);
+            softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
             pv_half<D, G>(S0 + GG::TILE, k0, pk, o, la);
         }
         // the barrier of pair p sits in step 4p + 3, as in attend8
@@ -906,8 +916,9 @@ constexpr int fwd_lds_bytes() {
 
 // W waves of 16*G rows each; two waves per SIMD (<= 256 registers per lane):
 // two 4-wave workgroups or one 8-wave workgroup per CU.
-template <int D, int G, int W>
+template <int D, int G, int W, bool PMAX>
 __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
+    constexpr int RF = PMAX ? kFixedPmax : kFixed;      // this kernel's fixed route
     using GG = Geo<D>;
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     static_assert(G * D <= 256, "a wave's accumulators and query fragments fit 256 registers");
@@ -1022,28 +1033,38 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
 #pragma unroll
     for (int g = 0; g < G; ++g) shift[g] *= c;
 
+    float m[G];
     if (split) {
-        float m[G];
         if (W == 8) {
             if (fixed)
-                attend_split8<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+                attend_split8<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
             else
-                attend_split8<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+                attend_split8<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
         } else {
             if (fixed)
-                attend_split<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+                attend_split<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
             else
-                attend_split<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+                attend_split<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
         }
-        if (!combine_split<D, G, W>(smem, o, rs, m, c, fixed, uwave, lane)) return;
     } else if (W == 8) {
-        if (fixed) attend8<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
-        else attend8<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+        if (fixed) attend8<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        else attend8<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
     } else if (fixed) {
-        attend<D, G, true>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+        attend<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
     } else {
-        attend<D, G, false>(smem, sl, Kh, Vh, qf, shift, c, o, rs, uwave, lane);
+        attend<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
     }
+    if (PMAX && fixed) {
+        // the largest probability this wave formed (every lane holds p >= 0,
+        // so the float bits order like unsigned integers)
+        float pm = m[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) pm = fmaxf(pm, m[g]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) pm = fmaxf(pm, __shfl_xor(pm, off, 64));
+        if (lane == 0 && pm > 0.f) atomicMax(p.pmax, __float_as_uint(pm));
+    }
+    if (split && !combine_split<D, G, W>(smem, o, rs, m, c, fixed, uwave, lane)) return;
 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -1126,8 +1147,11 @@ __global__ __launch_bounds__(64) void fwd_f32(const FwdArgs p) {
 }
 
 template <int D, int G, int W>
-void launch_bf16(const FwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_bf16<D, G, W>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
+void launch_bf16(const FwdArgs& a, bool pmax, hipStream_t stream) {
+    if (pmax)
+        hipLaunchKernelGGL((fwd_bf16<D, G, W, true>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fwd_bf16<D, G, W, false>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
 }
 
 }  // namespace
@@ -1150,6 +1174,9 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
     a.elig = reinterpret_cast<const uint8_t*>(ws + p.ws.elig);
     a.eligf = reinterpret_cast<const uint8_t*>(ws + p.ws.eligf);
     a.dslice = reinterpret_cast<const float*>(ws + p.ws.dslice);
+    a.pmax = reinterpret_cast<unsigned*>(const_cast<char*>(ws) + p.ws.pmax);
+    const bool pmax = (mode & FSA_MODE_RECORD_PMAX) != 0;
+    mode &= ~FSA_MODE_RECORD_PMAX;
     a.c = scale * kLog2e;
     a.N = s.F * s.T;
     a.NK = int32_t(p.key_tokens());
@@ -1177,13 +1204,13 @@ fsa_status launch_forward(const fsa_plan& p, const void* Q, const void* K, const
         a.nwg = int32_t(p.forward.workgroups);
         const int G = p.forward.granules, W = p.forward.waves;
         if (s.d == 128 && G == 2 && W == 8) {
-            launch_bf16<128, 2, 8>(a, stream);
+            launch_bf16<128, 2, 8>(a, pmax, stream);
         } else if (s.d == 128 && G == 2 && W == 4) {
-            launch_bf16<128, 2, 4>(a, stream);
+            launch_bf16<128, 2, 4>(a, pmax, stream);
         } else if (s.d == 64 && G == 2 && W == 8) {
-            launch_bf16<64, 2, 8>(a, stream);
+            launch_bf16<64, 2, 8>(a, pmax, stream);
         } else if (s.d == 64 && G == 2 && W == 4) {
-            launch_bf16<64, 2, 4>(a, stream);
+            launch_bf16<64, 2, 4>(a, pmax, stream);
         } else {
             set_error("fsa_forward: no kernel for d=%d with %d granules and %d waves", s.d, G, W);
             return FSA_ERR_UNSUPPORTED;

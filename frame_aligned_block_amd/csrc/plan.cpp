@@ -232,6 +232,7 @@ fsa_status create_plan(const fsa_shape* s_in, int32_t M, fsa_plan** out, const c
         w.statf = off;   off = align_up(off + BH * s.F * 4);
         w.eligf = off;   off = align_up(off + BH * s.F);
         w.dslice = off;  off = align_up(off + BH * s.F * s.d * 4);
+        w.pmax = off;    off = align_up(off + 4);
         const size_t nkparts = size_t(p->bounds.k.count()), nqparts = size_t(p->bounds.q.count());
         p->bounds.colsum = off;  off = align_up(off + BH * nkparts * s.d * 4);
         p->bounds.partmax = off; off = align_up(off + BH * nkparts * 4);

@@ -38,6 +38,7 @@ FSA_MODE_ONLINE_ONLY = 1
 FSA_MODE_FIXED_ONLY = 2
 FSA_MODE_AUTO_FRAME = 3
 FSA_MODE_AUTO_ROWS = 4
+FSA_MODE_RECORD_PMAX = 0x100
 MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MODE_FIXED_ONLY,
          "auto_frame": FSA_MODE_AUTO_FRAME, "auto_rows": FSA_MODE_AUTO_ROWS}
 
@@ -65,7 +66,7 @@ class fsa_shape(ctypes.Structure):
 
 class fsa_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("mu", "qnorm", "rframe", "rslice", "stat",
-                                         "elig", "statf", "eligf", "dslice", "total")]
+                                         "elig", "statf", "eligf", "dslice", "pmax", "total")]
 
 
 class FsaError(RuntimeError):
@@ -449,4 +450,5 @@ def workspace_views(plan: Plan, ws):
         "statf": view(lay["statf"], BH * s.F, torch.float32, 4, (s.B, s.H, s.F)),
         "eligf": view(lay["eligf"], BH * s.F, torch.uint8, 1, (s.B, s.H, s.F)),
         "dslice": view(lay["dslice"], BH * s.F * s.d, torch.float32, 4, (s.B, s.H, s.F, s.d)),
+        "pmax": view(lay["pmax"], 1, torch.float32, 4, (1,)),
     }

@@ -87,9 +87,14 @@ typedef enum {
     FSA_MODE_AUTO_FRAME = 3,    /* per (head, frame): fixed max where every row of
                                    the frame has its bound within FSA_ELIG_BETA,
                                    else online                                   */
-    FSA_MODE_AUTO_ROWS = 4      /* per block of query rows: fixed max where every
+    FSA_MODE_AUTO_ROWS = 4,     /* per block of query rows: fixed max where every
                                    row of the block has its gap bound within
                                    FSA_GAP_LIMIT, else online                    */
+    FSA_MODE_RECORD_PMAX = 0x100 /* flag OR'ed into a mode (bf16 plans): the
+                                   forward also records the largest probability
+                                   its fixed route forms into the workspace's
+                                   pmax (a check that the fixed shift bounds
+                                   every logit: it must not exceed 1 + 2^-8)   */
 } fsa_mode;
 
 /* Eligibility threshold on a head's largest row bound, in logit units. */
@@ -130,6 +135,10 @@ typedef struct {
     size_t eligf;   /* 1 if statf <= FSA_ELIG_BETA else 0, uint8 [B][H][F]     */
     size_t dslice;  /* mean key of the slice S(f) minus mu, float [B][H][F][d]
                        (a cross plan: the mean of all M keys minus their mu)   */
+    size_t pmax;    /* float [1]: the largest probability the fixed route formed
+                       (before rounding to bf16) in the forward launches run
+                       with FSA_MODE_RECORD_PMAX since fsa_bounds last wrote
+                       ws (which sets it to 0)                                 */
     size_t total;   /* bytes needed (== fsa_workspace_bytes)                   */
 } fsa_ws_layout;
 

@@ -16,6 +16,21 @@ BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
 F32_MAX_ABS = 1e-5
 
+# Regression bounds per workload (max-abs, mean-abs, relative L2 of the
+# output against the oracle), about 4x the errors the HIP path measured on the
+# GPU over the rows each test checks (tiny, small: every row; the full-size
+# workloads: the sampled rows of the listed heads together), capped by the
+# tolerances above. Relative L2 is dominated by rounding O to bf16 (about
+# 2.3e-3 measured), so its bound is twice that.
+REGRESSION = {
+    "tiny": (4e-6, 2e-7, 2e-6),
+    "small": (3e-3, 2e-4, 5e-3),
+    "720p": (8e-4, 1e-4, 5e-3),
+    "1080p": (7e-4, 8e-5, 5e-3),
+    "stress": (2e-2, 4.5e-4, 4e-3),
+    "720p-dense": (6e-4, 6e-5, 5e-3),
+}
+
 
 def say(*a):
     """Name the case before each GPU step (flushed, so a dying box still shows it)."""
@@ -94,6 +109,23 @@ def errors(got: torch.Tensor, want: np.ndarray):
     g = got.detach().to("cpu", torch.float64).numpy()
     diff = np.abs(g - want)
     return float(diff.max()), float(diff.mean()), bool(np.isfinite(g).all())
+
+
+def rel_l2(got: torch.Tensor, want: np.ndarray) -> float:
+    """||O - O_ref|| / ||O_ref|| over the given rows."""
+    g = got.detach().to("cpu", torch.float64).numpy()
+    return float(np.linalg.norm(g - want) / np.linalg.norm(want))
+
+
+def assert_regression(name: str, got: torch.Tensor, want: np.ndarray, what: str):
+    """The measured-error band of a workload (REGRESSION), reported as well."""
+    mx, mean, finite = errors(got, want)
+    rl = rel_l2(got, want)
+    print(f"{what}: max {mx:.3g} mean {mean:.3g} rel_l2 {rl:.3g}")
+    bmax, bmean, brl = REGRESSION[name]
+    assert finite and mx <= bmax and mean <= bmean and rl <= brl, \
+        f"{what}: max {mx:.3g} mean {mean:.3g} rel_l2 {rl:.3g} outside ({bmax}, {bmean}, {brl})"
+    return mx, mean, rl
 
 
 def assert_close(cfg: Config, got: torch.Tensor, want: np.ndarray, what: str):

@@ -267,3 +267,19 @@ def test_attention_rejects_bad_out_and_workspace():
     with pytest.raises(ValueError):
         fsa._check_out_ws(None, torch.zeros(8, dtype=torch.uint8), q, 1024)   # not on a GPU
     fsa._check_out_ws(None, None, q, 1024)                                 # nothing given
+
+
+def test_record_pmax_flag_validation():
+    """FSA_MODE_RECORD_PMAX combines with any route of a bf16 plan; an fp32
+    plan rejects it, and unknown mode bits are rejected, before any launch."""
+    p = fsa.fsa_plan_create(shape())                  # fp32
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE * 64, FAKE * 96, FAKE * 128, 0.125,
+                        fsa.FSA_MODE_AUTO | fsa.FSA_MODE_RECORD_PMAX, 0)
+    assert e.value.status == fsa.FSA_ERR_UNSUPPORTED
+    for bad in (fsa.FSA_MODE_AUTO | 0x200, 5 | fsa.FSA_MODE_RECORD_PMAX):
+        with pytest.raises(fsa.FsaError) as e:
+            fsa.fsa_forward(p, FAKE, FAKE * 32, FAKE * 64, FAKE * 96, FAKE * 128, 0.125, bad, 0)
+        assert e.value.status == fsa.FSA_ERR_INVALID_ARG
+    lay = fsa.fsa_workspace_layout(p)
+    assert lay["pmax"] % 256 == 0 and lay["pmax"] + 4 <= lay["total"]

@@ -14,8 +14,8 @@ from oracle import fsa_oracle as orc
 from frame_aligned_block_amd import fsa
 from frame_aligned_block_amd.inputs import CONFIGS, to_f64
 
-from gpu_util import (BF16_MAX_ABS, Run, assert_close, errors, oracle_rows, sample_rows,
-                      say)
+from gpu_util import (BF16_MAX_ABS, BF16_MEAN_ABS, Run, assert_close, assert_regression, errors,
+                      oracle_rows, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,7 @@ def test_tiny_fp32_full():
     for mode in ("auto", "online", "fixed"):
         O = run.forward(mode)
         assert_close(cfg, O, want, f"tiny {mode}")
+        assert_regression("tiny", O, want, f"tiny {mode}")
 
 
 @pytest.mark.parametrize("row_block", ROW_BLOCKS)
@@ -106,10 +107,11 @@ def test_small_bf16_full(row_block):
     O = run.forward("auto")
     Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
     want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
-    mx, mean = assert_close(cfg, O, want, "small auto")
-    print(f"small auto: max {mx:.3g} mean {mean:.3g}")
+    assert_close(cfg, O, want, "small auto")
+    assert_regression("small", O, want, f"small auto {row_block}")
     O2 = run.forward("online")
     assert_close(cfg, O2, want, "small online")
+    assert_regression("small", O2, want, f"small online {row_block}")
 
 
 # ------------------------------------------------------------------ forward, full size sampled
@@ -125,11 +127,14 @@ def test_full_size_sampled(name, heads, row_block):
     run = Run(cfg, row_block=row_block).bounds()
     O = run.forward("auto")
     assert bool(torch.isfinite(O).all())
+    got, wants = [], []
     for h in heads:
         rows = sample_rows(cfg, 150, seed=h)
         want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
-        mx, mean = assert_close(cfg, O[0, h, rows], want, f"{name} head {h}")
-        print(f"{name} h{h}: max {mx:.3g} mean {mean:.3g}")
+        assert_close(cfg, O[0, h, rows], want, f"{name} head {h}")
+        got.append(O[0, h, rows])
+        wants.append(want)
+    assert_regression(name, torch.cat(got), np.concatenate(wants), f"{name} heads {heads}")
     if name == "stress":
         v = run.views()
         assert int(v["elig"][0, 7]) == 0 and int(v["elig"][0, 6]) == 1
@@ -365,3 +370,64 @@ def test_split_workgroups_exact_and_deterministic(row_block):
             want = oracle_rows(cfg, run.Q, run.K, run.V, 0, h, rows)
             mx, mean = assert_close(cfg, outs[0][0, h, rows], want, f"split rows {mode} head {h}")
             print(f"split rows {mode} h{h}: max {mx:.3g} mean {mean:.3g}")
+
+
+# ------------------------------------------------------------------ negative controls
+
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
+def test_negative_controls_fail_the_bar(row_block):
+    """The kernel run with the wrong slice must fail the bar against the
+    oracle's window +-2 + reference frame 0 (so the bar can see a mask error):
+    window +-1 on every row, and the reference frame dropped on frames 3-6 (a
+    launch with reference frame 4, which those frames' windows already hold,
+    gives them the window alone). The oracle puts both at mean-abs 8e-3 to
+    1.3e-2 here, against the bar's 2e-3; the right launch passes it."""
+    cfg = CONFIGS["small"].with_(H=2)
+    say("negative controls", row_block)
+    run = Run(cfg, row_block=row_block).bounds()
+    Q, K, V = (to_f64(t) for t in (run.Q, run.K, run.V))
+    want = orc.attention(Q, K, V, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    assert_close(cfg, run.forward(), want, "the right slice")
+    rows = np.arange(3 * cfg.T, 7 * cfg.T)
+    for what, window, ref, sel in (("window +-1", 1, 0, slice(None)),
+                                   ("reference frame dropped", cfg.window, 4, rows)):
+        bad = Run(cfg.with_(window=window, ref_frame=ref), inputs=(run.Q, run.K, run.V),
+                  row_block=row_block).bounds()
+        O = bad.forward()
+        mx, mean, finite = errors(O[:, :, sel], want[:, :, sel])
+        print(f"{what}: max {mx:.3g} mean {mean:.3g}")
+        assert finite and (mx > BF16_MAX_ABS or mean > BF16_MEAN_ABS), what
+        assert mean > 2 * BF16_MEAN_ABS, what          # by a clear margin
+
+
+# ------------------------------------------------------------------ largest probability
+
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
+def test_fixed_route_probability_is_at_most_one(row_block):
+    """The fixed max bounds every logit of its row (Cauchy-Schwarz on the
+    centred keys), so no probability the fixed route forms exceeds 1; with
+    FSA_MODE_RECORD_PMAX the kernel records the largest one. It must be at
+    most 1 + 2^-8 (fp32 rounding of the scores and the shift), equal the
+    oracle's max over rows of exp(max_j s_ij - B_i) to fp32 rounding, and the
+    recording must leave the output bit-identical."""
+    cfg = CONFIGS["small"].with_(H=2)
+    say("largest fixed-route probability", row_block)
+    run = Run(cfg, row_block=row_block).bounds()
+    O = run.forward("auto")
+    O_rec = run.forward(fsa.FSA_MODE_AUTO | fsa.FSA_MODE_RECORD_PMAX)
+    assert torch.equal(O, O_rec)
+    pmax = float(run.views()["pmax"][0])
+    Q, K = to_f64(run.Q), to_f64(run.K)
+    b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    want = 0.0
+    for h in range(cfg.H):
+        kc = K[0, h] - b["mu"][0, h]
+        for f in range(cfg.F):
+            keys = orc.slice_keys(cfg.F, cfg.T, cfg.window, cfg.ref_frame, f)
+            rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
+            s = cfg.scale * Q[0, h, rows] @ kc[keys].T
+            B = cfg.scale * b["qnorm"][0, h, rows] * b["R_S"][0, h, f]
+            want = max(want, float(np.exp(s.max(axis=1) - B).max()))
+    print(f"largest fixed-route p: {pmax:.6g} (oracle {want:.6g})")
+    assert 0.0 < pmax <= 1.0 + 2.0 ** -8
+    assert pmax == pytest.approx(want, rel=2e-3)

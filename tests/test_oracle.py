@@ -533,3 +533,36 @@ def test_cross_eligibility_by_construction():
             assert stat < orc.BETA / margin and b["elig"][0, 0], (name, h, stat)
             raw = cfg.scale * np.linalg.norm(Q[0, 0], axis=1).max() * np.linalg.norm(K[0, 0], axis=1).max()
             assert raw > orc.BETA * margin, (name, h, raw)
+
+
+@pytest.mark.parametrize("F,T,M,bq,bk", [(3, 48, 80, 16, 16), (4, 96, 48, 32, 48),
+                                         (2, 160, 320, 80, 64), (5, 16, 16, 16, 16)])
+def test_cross_plan_against_bruteforce_tiles_and_closed_forms(F, T, M, bq, bk):
+    """cross_plan against the definition written out pair by pair: a tile is
+    live iff some (query, reference key) pair in it attends, and in
+    cross-attention every pair does, so the live set is the full grid of
+    (F*T/bq) x (M/bk) tiles; each q-block's frame is floor(qb*bq / T) and its
+    one key run is the whole set [0, M)."""
+    p = orc.cross_plan(F, T, M, bq, bk)
+    nqb, nkb = F * T // bq, M // bk
+    live = np.zeros((nqb, nkb), dtype=bool)
+    for i in range(F * T):              # brute force over every pair
+        for j in range(M):
+            live[i // bq, j // bk] = True
+    rows, cols = np.nonzero(live)        # row-major: ascending qb, then kb
+    assert p["nnz"] == rows.size == nqb * nkb
+    assert np.array_equal(p["col_idx"], cols)
+    assert np.array_equal(p["row_ptr"], np.searchsorted(rows, np.arange(nqb + 1)))
+    assert np.array_equal(p["qframe"], [(qb * bq) // T for qb in range(nqb)])
+    assert p["runs"] == [[(0, M)]] * nqb
+
+
+@pytest.mark.parametrize("F,T,bq,bk", [(3, 48, 16, 48), (4, 32, 32, 16), (2, 96, 48, 32)])
+def test_cross_plan_equals_the_dense_self_plan(F, T, bq, bk):
+    """Two independent routes to one tile list: cross-attention to a reference
+    set of M = F*T keys and self-attention whose window covers every frame both
+    make every tile live, so their CSR arrays and q-block frames agree."""
+    c = orc.cross_plan(F, T, F * T, bq, bk)
+    s = orc.plan(F, T, F - 1, 0, bq, bk)
+    for k in ("row_ptr", "col_idx", "qframe"):
+        assert np.array_equal(np.asarray(c[k]), np.asarray(s[k])), k

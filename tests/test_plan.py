@@ -87,7 +87,10 @@ def test_cross_plan_bit_exact_vs_oracle(F, T, M, bq, bk):
     assert np.array_equal(got["row_ptr"], want["row_ptr"])
     assert np.array_equal(got["col_idx"], want["col_idx"])
     assert np.array_equal(got["qframe"], want["qframe"])
-    assert np.all(got["runs"] == np.array([0, M, 0, 0]))
+    # the oracle's key runs, in the library's {start0, end0, start1, end1} form
+    runs = np.array([[a, e] + [0, 0] * (2 - len(r)) for r in want["runs"] for a, e in r[:1]])
+    assert len(want["runs"]) == got["n_qblocks"] and all(len(r) == 1 for r in want["runs"])
+    assert np.array_equal(got["runs"], runs)
     assert fsa.fsa_plan_valid_pairs(p) == F * T * M
     assert fsa.fsa_plan_key_tokens(p) == M
 
