@@ -66,52 +66,92 @@ def measured_traffic(config: str):
     return float(tb.group(1))
 
 
-def cpu_baseline(cfg, Q, K, V, seconds: float):
-    """The fp64 oracle, as it stands, on whole (head, frame) blocks of the
-    same workload until about `seconds` of CPU work; valid TFLOP/s."""
+# Largest worker pool the oracle's timing may use: the GPU machine's host share
+# (one GPU's 16 cores), whatever the host reports beyond it.
+MAX_CPU_WORKERS = 16
+
+
+def _oracle_worker_init():
+    """One BLAS thread per worker process (set before numpy loads)."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+_HEADS = {}
+
+
+def _oracle_block(task):
+    """One (head, query frame) block of a workload through the fp64 oracle, on
+    one core: (seconds, valid FLOPs). The head is drawn on the host by the
+    same seeded recipe as the GPU inputs (the host and device generators give
+    different values; the work is the same)."""
     import numpy as np
     from oracle import fsa_oracle as orc
-    from frame_aligned_block_amd.inputs import to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"]
-                      or [1])
-    except Exception:   # noqa: BLE001
-        threads = 1
-    # heaviest frames first, cycling over heads
+    from frame_aligned_block_amd.inputs import CONFIGS, make_head, to_f64
+    name, h, f = task
+    cfg = CONFIGS[name]
+    if (name, h) not in _HEADS:
+        _HEADS.clear()
+        _HEADS[(name, h)] = tuple(to_f64(t)[None, None] for t in make_head(cfg, 0, 0, h))
+    q, k, v = _HEADS[(name, h)]
+    rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
+    t0 = time.perf_counter()
+    orc.attention_rows(q, k, v, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0, 0, rows)
+    dt = time.perf_counter() - t0
+    keys = cfg.T * len(orc.slice_frames(cfg.F, cfg.window, cfg.ref_frame, f))
+    return dt, 4.0 * cfg.d * cfg.T * keys
+
+
+def _blocks(cfg, heads, per_head=None):
+    """(head, frame) blocks of the given heads, head by head, each head's
+    heaviest frames first (per_head of them, or all)."""
+    from oracle import fsa_oracle as orc
     frames = sorted(range(cfg.F), key=lambda f: -len(orc.slice_frames(cfg.F, cfg.window,
                                                                        cfg.ref_frame, f)))
-    units = [(h, f) for f in frames for h in range(cfg.H)]
+    return [(cfg.name, h % cfg.H, f) for h in heads for f in frames[:per_head]]
 
-    def keys_of(f):       # keys a query of frame f attends to
-        return cfg.M if cfg.M else cfg.T * len(orc.slice_frames(cfg.F, cfg.window,
-                                                                cfg.ref_frame, f))
-    cache = {}
-    flops = 0.0
-    spent = 0.0
-    n = 0
-    for h, f in units:
-        if spent >= seconds:
-            break
-        if h not in cache:
-            cache.clear()
-            cache[h] = tuple(to_f64(t[0, h])[None, None] for t in (Q, K, V))
-        q, k, v = cache[h]
-        rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
+
+def cpu_baseline(cfg, total_flops: float, heads: int = 0, small_heads: int = 0):
+    """The fp64 oracle as it stands, on the host's cores: one whole call of the
+    workload (or its first `heads` heads, scaled to a call) on a pool of one
+    process per core (at most MAX_CPU_WORKERS), one BLAS thread each, each
+    worker taking one head's (head, query frame) blocks at a time; and one
+    whole call of the small workload on one core (or its first `small_heads`
+    heads, scaled). None for the cross-attention and producer workloads."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    from frame_aligned_block_amd.inputs import CONFIGS
+    if cfg.M or cfg.grid:
+        return None
+    cores = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+    ctx = mp.get_context("spawn")          # a fresh interpreter: nothing of the GPU is inherited
+    nh = min(cfg.H, max(heads, cores)) if heads else cfg.H    # at least one head per worker
+    tasks = _blocks(cfg, range(nh))
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx,
+                                initializer=_oracle_worker_init) as pool:
+        list(pool.map(_oracle_block, [(cfg.name, 0, cfg.F // 2)] * cores))   # imports, warm-up
         t0 = time.perf_counter()
-        if cfg.M:
-            orc.cross_attention_rows(q, k, v, cfg.scale, 0, 0, rows)
-        else:
-            orc.attention_rows(q, k, v, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale, 0,
-                               0, rows)
-        spent += time.perf_counter() - t0
-        flops += 4.0 * cfg.d * cfg.T * keys_of(f)
-        n += 1
-    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} (head, query-frame) blocks of {cfg.T} rows each of the {cfg.name} "
-                      f"workload (heaviest frames first), {flops / 1e9:.0f} valid GFLOP in "
-                      f"{spent:.1f} s; fp64 numpy, BLAS on {threads} threads"}
+        res = list(pool.map(_oracle_block, tasks, chunksize=cfg.F))
+        wall = time.perf_counter() - t0
+    flops = sum(r[1] for r in res)
+    rate = flops / wall
+    small = CONFIGS["small"]
+    sh = small_heads or small.H
+    with cf.ProcessPoolExecutor(max_workers=1, mp_context=ctx,
+                                initializer=_oracle_worker_init) as one:
+        list(one.map(_oracle_block, [(small.name, 0, 0)]))                 # imports, warm-up
+        t0 = time.perf_counter()
+        list(one.map(_oracle_block, _blocks(small, range(sh)), chunksize=small.F))
+        s_wall = time.perf_counter() - t0
+    scaled = " (scaled to all heads)" if nh < cfg.H else ""
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "ms_per_call": round(total_flops / rate * 1e3, 1),
+            "small_single_core_ms_per_call": round(s_wall * small.H / sh * 1e3, 1),
+            "sample": f"{nh} of {cfg.H} heads of the {cfg.name} workload ({len(tasks)} (head, "
+                      f"query-frame) blocks, {flops / 1e9:.0f} of {total_flops / 1e9:.0f} valid "
+                      f"GFLOP) in {wall:.1f} s wall on a pool of {cores} processes, one BLAS "
+                      f"thread each, fp64 numpy{scaled}; the small workload on one core: {sh} of "
+                      f"{small.H} heads in {s_wall:.1f} s" + (" (scaled)" if sh < small.H else "")}
 
 
 def workload_name(cfg) -> str:
@@ -245,6 +285,46 @@ def bench_producer(args, cfg) -> int:
     return 0
 
 
+def extra_workload(name: str, launches: int = 5):
+    """Forward time of another workload in the same process (not part of the
+    timed step): the median of `launches` event-timed launches after two
+    warm-ups, its valid-FLOP rate and fraction of peak, the eligible fraction,
+    and for mixed-route workloads the same forward with every head online."""
+    import torch
+    from frame_aligned_block_amd import fsa
+    from frame_aligned_block_amd.inputs import CONFIGS, make_inputs
+    cfg = CONFIGS[name]
+    print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
+    Q, K, V = make_inputs(cfg, seed=0, device="cuda")
+    plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d, cfg.window,
+                                              cfg.ref_frame, 0, 0, fsa.FSA_BF16))
+    ws = torch.zeros(fsa.fsa_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
+    O = torch.empty_like(Q)
+    flops = 4.0 * cfg.d * fsa.fsa_plan_valid_pairs(plan) * cfg.B * cfg.H
+    stream = torch.cuda.current_stream()
+    fsa.fsa_bounds(plan, Q, K, ws, cfg.scale, stream)
+    out = {"workload": workload_name(cfg), "row_block": fsa.fsa_plan_row_block(plan),
+           "valid_flops": flops}
+    for mode in (["auto", "online"] if cfg.loose_period else ["auto"]):
+        for _ in range(2):
+            fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, mode, stream)
+        ms = timed(lambda: fsa.fsa_forward(plan, Q, K, V, O, ws, cfg.scale, mode, stream),
+                   launches, stream)
+        key = "forward_ms_median" if mode == "auto" else "online_only_forward_ms_median"
+        out[key] = round(ms, 4)
+        if mode == "auto":
+            out["tflops"] = round(flops / ms / 1e9, 2)
+            out["frac"] = round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+    if "online_only_forward_ms_median" in out:
+        out["fixed_max_speedup"] = round(out["online_only_forward_ms_median"]
+                                         / out["forward_ms_median"], 4)
+    el = fsa.fsa_copy_eligibility(plan, ws, stream)
+    out["eligible_heads"] = f"{int(el.sum())}/{el.size}"
+    del Q, K, V, O, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,10 +334,14 @@ def main() -> int:
     ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed", "auto_frame", "auto_rows"])
     ap.add_argument("--ab-launches", type=int, default=5,
                     help="timed online-only forward launches for the A/B figure")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="time the oracle on this many heads and scale (0: the whole call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bq", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--extra", default="stress,1080p",
+                    help="other workloads whose forward is timed after the 720p line's "
+                         "(comma list; empty for none)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -361,6 +445,7 @@ def main() -> int:
                    "B": cfg.B, "H": cfg.H, "F": cfg.F, "T": cfg.T, "d": cfg.d,
                    **({"M": cfg.M} if cfg.M else {}),
                    "mode": args.mode, "bq": fsa.fsa_plan_shape(plan).bq,
+                   "row_block": fsa.fsa_plan_row_block(plan),
                    "valid_pairs_per_head": pairs, "valid_flops_per_step": flops},
         "ms_per_call": round(ms_step, 4),
         "pct_bf16_peak": round(100.0 * flops / ms_step / 1e9 / PEAK_BF16_TFLOPS, 2),
@@ -377,9 +462,11 @@ def main() -> int:
                      "traffic": measured_traffic(cfg.name)},
         "cpu_baseline": None,
     }
+    if args.config == "720p" and args.extra:
+        line["workloads"] = {n: extra_workload(n) for n in args.extra.split(",") if n}
     if not args.no_cpu_baseline:
-        print(f"[bench] oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, args.cpu_seconds)
+        print("[bench] oracle baseline on the host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, flops, args.cpu_heads)
     print(json.dumps(line), flush=True)
     return 0
 
