@@ -213,10 +213,10 @@ extern "C" size_t fsa_attention_workspace_bytes(int32_t F, int32_t T, int32_t wi
 
 namespace {
 
-// bounds then forward with a cached plan; M > 0: cross-attention.
-fsa_status attend(const char* who, const void* Q, const void* K, const void* V, void* O,
-                  const fsa_shape& shape, int32_t M, float scale, int32_t mode, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
+// Checks of Q, K, V, O, scale and mode shared by the calls that run bounds
+// then forward (before a plan is at hand).
+fsa_status check_call(const char* who, const void* Q, const void* K, const void* V,
+                      const void* O, float scale, int32_t mode) {
     if (!Q || !K || !V || !O) {
         set_error("%s: NULL Q, K, V or O", who);
         return FSA_ERR_INVALID_ARG;
@@ -230,10 +230,15 @@ fsa_status attend(const char* who, const void* Q, const void* K, const void* V, 
         set_error("%s: unknown mode %d", who, mode);
         return FSA_ERR_INVALID_ARG;
     }
-    PlanRef ref;
-    fsa_status st = cached_plan(shape, M, &ref);
-    if (st != FSA_OK) return st;
-    const fsa_plan* p = ref.get();
+    return FSA_OK;
+}
+
+// bounds then forward on a plan, every argument validated before either
+// launch.
+fsa_status attend_plan(const char* who, const fsa_plan* p, const void* Q, const void* K,
+                       const void* V, void* O, float scale, int32_t mode, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    fsa_status st;
     if (!ws || ws_bytes < p->ws.total) {
         set_error("%s: workspace of %zu bytes, %zu needed", who, ws ? ws_bytes : size_t(0),
                   p->ws.total);
@@ -260,6 +265,18 @@ fsa_status attend(const char* who, const void* Q, const void* K, const void* V, 
     st = fsa_bounds(p, Q, K, ws, scale, stream);
     if (st != FSA_OK) return st;
     return fsa_forward(p, Q, K, V, O, ws, scale, mode, stream);
+}
+
+// bounds then forward with a cached plan; M > 0: cross-attention.
+fsa_status attend(const char* who, const void* Q, const void* K, const void* V, void* O,
+                  const fsa_shape& shape, int32_t M, float scale, int32_t mode, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    fsa_status st = check_call(who, Q, K, V, O, scale, mode);
+    if (st != FSA_OK) return st;
+    PlanRef ref;
+    st = cached_plan(shape, M, &ref);
+    if (st != FSA_OK) return st;
+    return attend_plan(who, ref.get(), Q, K, V, O, scale, mode, ws, ws_bytes, stream);
 }
 
 }  // namespace
