@@ -1,6 +1,8 @@
 // C-ABI layer of libfsa: argument validation, error reporting, and the
 // per-shape plan cache behind fsa_attention. Kernels live in bounds.hip and
 // forward.hip; the plan builder in plan.cpp.
+#include <hip/hip_runtime.h>
+
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -311,6 +313,70 @@ extern "C" fsa_status fsa_cross_attention(const void* Q, const void* Kr, const v
     }
     return attend("fsa_cross_attention", Q, Kr, Vr, O, make_shape(F, T, 0, 0, B, H, d, dtype), M,
                   scale, mode, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ static workspace
+
+// The workspace of fsa_attention_static: one file-scope device array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends. Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): the address comes from
+// hipGetSymbolAddress, taken once per device with that device current, on
+// the device's first call.
+static __device__ __align__(256) unsigned char scratch[FSA_STATIC_WS_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of scratch, or an error status.
+fsa_status static_workspace(void** out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_error("fsa_attention_static: no usable current device (%s, device %d)",
+                  hipGetErrorString(err), dev);
+        return FSA_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr) {
+            set_error("fsa_attention_static: address of the static workspace on device %d: %s",
+                      dev, hipGetErrorString(err));
+            return FSA_ERR_HIP;
+        }
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return FSA_OK;
+}
+
+}  // namespace
+
+extern "C" fsa_status fsa_attention_static(const fsa_plan* plan, const void* Q, const void* K,
+                                           const void* V, void* O, float scale, int32_t mode,
+                                           hipStream_t stream) {
+    const char* who = "fsa_attention_static";
+    if (!plan) {
+        set_error("%s: NULL plan", who);
+        return FSA_ERR_INVALID_ARG;
+    }
+    if (plan->ws.total > FSA_STATIC_WS_BYTES) {
+        set_error("%s: the plan needs a workspace of %zu bytes, above the static workspace's "
+                  "%zu (use fsa_attention with a workspace of its own)", who, plan->ws.total,
+                  size_t(FSA_STATIC_WS_BYTES));
+        return FSA_ERR_WORKSPACE;
+    }
+    fsa_status st = check_call(who, Q, K, V, O, scale, mode);
+    if (st != FSA_OK) return st;
+    void* ws = nullptr;
+    st = static_workspace(&ws);
+    if (st != FSA_OK) return st;
+    return attend_plan(who, plan, Q, K, V, O, scale, mode, ws, FSA_STATIC_WS_BYTES, stream);
 }
 
 // ------------------------------------------------------------------ producer

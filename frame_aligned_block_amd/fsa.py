@@ -45,6 +45,7 @@ MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MOD
 FSA_ELIG_BETA = 32.0
 FSA_GAP_LIMIT = 64.0
 FSA_MAX_FRAMES = 255
+FSA_STATIC_WS_BYTES = 16 << 20
 
 # Every symbol include/fsa.h declares.
 EXPORTS = (
@@ -52,7 +53,7 @@ EXPORTS = (
     "fsa_plan_export", "fsa_plan_valid_pairs", "fsa_plan_key_tokens", "fsa_plan_row_block",
     "fsa_plan_set_row_block", "fsa_workspace_bytes",
     "fsa_workspace_layout", "fsa_bounds", "fsa_forward", "fsa_copy_eligibility",
-    "fsa_attention", "fsa_attention_workspace_bytes", "fsa_cross_attention",
+    "fsa_attention", "fsa_attention_workspace_bytes", "fsa_attention_static", "fsa_cross_attention",
     "fsa_cross_attention_workspace_bytes", "fsa_prep_weight_bytes", "fsa_prep_pack_weights",
     "fsa_prep", "fsa_bounds_after_prep",
     "fsa_cache_clear", "fsa_status_string", "fsa_last_error",
@@ -119,6 +120,8 @@ def lib() -> ctypes.CDLL:
     L.fsa_attention.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, c_int32, c_float,
                                 c_int32, c_int32, c_int32, c_int32, c_int32, P, c_size_t, P]
     L.fsa_attention.restype = c_int32
+    L.fsa_attention_static.argtypes = [P, P, P, P, P, c_float, c_int32, P]
+    L.fsa_attention_static.restype = c_int32
     L.fsa_attention_workspace_bytes.argtypes = [c_int32] * 8
     L.fsa_attention_workspace_bytes.restype = c_size_t
     L.fsa_cross_attention.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, c_float, c_int32,
@@ -300,6 +303,13 @@ def fsa_attention(Q, K, V, O, F, T, window, ref_frame, scale, B, H, d, dtype, mo
     _check(lib().fsa_attention(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), F, T, window, ref_frame,
                                float(scale), B, H, d, dtype, mode, _ptr(ws), int(ws_bytes),
                                _stream(stream)))
+
+
+def fsa_attention_static(plan: Plan, Q, K, V, O, scale: float, mode=FSA_MODE_AUTO,
+                         stream=None) -> None:
+    mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().fsa_attention_static(plan, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), float(scale),
+                                      mode, _stream(stream)))
 
 
 def fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, dtype) -> int:

@@ -315,6 +315,26 @@ fsa_status fsa_cross_attention(const void* Q, const void* Kr, const void* Vr, vo
 size_t fsa_cross_attention_workspace_bytes(int32_t F, int32_t T, int32_t M, int32_t B, int32_t H,
                                            int32_t d, int32_t dtype);
 
+/*
+ * fsa_attention_static -- for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * fsa_bounds then fsa_forward on `plan` (made beforehand by
+ * fsa_plan_create or fsa_plan_create_cross, so this call allocates nothing,
+ * host or device), with a workspace that is a static device array of
+ * FSA_STATIC_WS_BYTES inside the library instead of the caller's. Each GPU
+ * holds its own copy until the process ends. Every call on a GPU shares that
+ * GPU's array and leaves its contents behind (nothing in it needs to start at
+ * zero: fsa_bounds writes every product the forward reads), so calls that
+ * overlap on one GPU (other threads, other streams) race; serialize them.
+ * Same arguments, layout and checks as fsa_attention with the plan given.
+ * Errors: FSA_ERR_WORKSPACE (the plan's workspace exceeds
+ * FSA_STATIC_WS_BYTES), FSA_ERR_HIP (no current device, or the array's
+ * address could not be taken), and those of fsa_bounds and fsa_forward.
+ */
+#define FSA_STATIC_WS_BYTES (16u << 20)
+fsa_status fsa_attention_static(const fsa_plan* plan, const void* Q, const void* K, const void* V,
+                                void* O, float scale, int32_t mode, hipStream_t stream);
+
 /* Drop every cached plan of fsa_attention and fsa_cross_attention. Safe to
    call while other threads are inside those calls: a call keeps the plan it
    looked up until it returns. */
