@@ -37,17 +37,26 @@ int32_t pick_bq(int32_t T) {
 // d = 128; d = 64 keeps the same 32 rows per wave.
 constexpr int32_t kGranules = 2;
 
-// Waves per workgroup of the bf16 forward kernel. 4-wave workgroups (128
-// rows, two per CU): the two waves that share a SIMD belong to different
-// workgroups, so one workgroup's barrier never lines them up, and one wave's
-// softmax keeps overlapping the other's products. 8-wave workgroups (256 rows,
-// one per CU) share each chunk's copies among twice the rows, but their
-// barriers align both waves of every SIMD; measured slower on every workload
-// (720p 9.41 against 8.98 ms, 1080p 21.3 against 20.3 ms, same process), so
-// they are chosen only on request (fsa_plan_set_row_block).
+// Waves per workgroup of the bf16 forward kernel, per shape ("Unchaining the
+// Softmax" ¶3 re-tunes block shapes together with the softmax).
+//  * 8-wave workgroups (256 rows, one per CU) stage each key chunk once for
+//    twice the rows, so the CU moves half the bytes from L2 into LDS and
+//    holds a higher clock under the chip's power limit (1.93 against 1.76
+//    GHz at 720p); but their barriers line up the two waves of every SIMD,
+//    which costs about as many cycles as the clock gains.
+//  * 4-wave workgroups (128 rows, two per CU): the two waves of a SIMD belong
+//    to different workgroups and stay out of phase.
+// Same-process measurements: 8 waves 0.6-1.6% faster on the 1080p-shaped
+// chunk (T = 8160: 255 row units per frame, every 8-wave workgroup full but
+// the last, one unit short); even at 720p (T = 3600: 113 units, the last
+// workgroup of each frame left with one unit); 4 waves 18% faster on the
+// small chunk (T = 880) and 1% on the cross workload. So 8 waves where frames
+// are large and fill 8-wave workgroups to within one unit, else 4.
 int32_t pick_waves(const fsa_shape& s) {
-    (void)s;
-    return 4;
+    const int32_t units = (s.T / 16 + kGranules - 1) / kGranules;
+    const bool large = units >= 128;                     // 16 or more 8-wave workgroups
+    const bool fills = units % 8 == 0 || units % 8 == 7;
+    return large && fills ? 8 : 4;
 }
 
 // k-block size of the tile list when the caller leaves it open: as pick_bq,

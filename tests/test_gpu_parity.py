@@ -19,8 +19,9 @@ from gpu_util import (BF16_MAX_ABS, BF16_MEAN_ABS, Run, assert_close, assert_reg
 
 pytestmark = pytest.mark.gpu
 
-# Workgroup geometries of the bf16 forward kernel: the plan's own choice (128
-# rows, 4 waves, for every bf16 shape here) and the 8-wave 256-row one.
+# Workgroup geometries of the bf16 forward kernel: 4 waves (128 rows, the
+# plan's choice for most shapes) and 8 waves (256 rows, its choice at 1080p);
+# every workload runs on both.
 ROW_BLOCKS = (128, 256)
 
 if not torch.cuda.is_available():   # collected on CPU too; every test here is gpu-marked
