@@ -285,15 +285,18 @@ __device__ __forceinline__ LaneAddr lane_addr(int ln, int lj) {
 
 // S^T for the 32 keys at chunk-local key koff (0 or 32): s[0] = first 16 keys,
 // s[1] = next 16; the lane holds query ln of each granule and keys 4lj..4lj+3.
+// The products accumulate onto s0 (per granule): zero, or on the scaled fixed
+// route minus the row's shift (its query fragments then carry the scale), so
+// that the scores come out as the exponents themselves.
 template <int D, int G, int NB>
 __device__ __forceinline__ void scores(const unsigned char* Ks, int koff,
-                                       const bf16x8 (&qf)[G][D / 32], f32x4 (&s)[2][G],
-                                       const LaneAddr& la) {
+                                       const bf16x8 (&qf)[G][D / 32], const f32x4 (&s0)[G],
+                                       f32x4 (&s)[2][G], const LaneAddr& la) {
     using GG = Geo<D>;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int g = 0; g < G; ++g) s[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < G; ++g) s[b][g] = s0[g];
 #pragma unroll
     for (int ks = 0; ks < GG::KS; ++ks) {
 #pragma unroll
@@ -332,18 +335,23 @@ __device__ __forceinline__ float sum_pairs(const bf16x2* pp, int n, float acc) {
 }
 
 // Routes of the slice walks (template parameter R).
-constexpr int kOnline = 0;      // running reference max
-constexpr int kFixed = 1;       // shift fixed at the row's Cauchy-Schwarz bound
-constexpr int kFixedPmax = 2;   // kFixed, also keeping each row's largest p in m
+constexpr int kOnline = 0;       // running reference max
+constexpr int kFixed = 1;        // shift fixed at the row's Cauchy-Schwarz bound
+constexpr int kFixedScaled = 2;  // kFixed on scaled query fragments, the shift in s0
+constexpr int kPmax = 4;         // flag on a fixed route: keep each row's largest p in m
+__host__ __device__ constexpr bool scaled_route(int r) { return (r & 3) == kFixedScaled; }
+__host__ __device__ constexpr bool pmax_route(int r) { return (r & kPmax) != 0; }
 
 // Probabilities of NK scores of one granule-row. Fixed route: the shift is
-// the row's Cauchy-Schwarz bound; kFixedPmax keeps the largest probability
-// formed (before rounding to bf16) in m, which the fixed route does not use
-// otherwise. Online route: a running reference max,
-// moved (with the accumulator and row sum rescaled) only when a step's max
-// exceeds it by more than kLazyLog2 in log2 units, and only in the steps
-// where some row of the wave needs it; until then the row's probabilities
-// may reach 2^kLazyLog2, which bf16 and the fp32 sums hold as precisely.
+// the row's Cauchy-Schwarz bound (scale folded in, log2 units); on the scaled
+// fixed route the scores already hold the exponents, so a probability is one
+// exp2. With kPmax the largest probability formed (before rounding to bf16)
+// is kept in m, which the fixed routes do not use otherwise. Online route: a
+// running reference max, moved (with the accumulator and row sum rescaled)
+// only when a step's max exceeds it by more than kLazyLog2 in log2 units, and
+// only in the steps where some row of the wave needs it; until then the
+// row's probabilities may reach 2^kLazyLog2, which bf16 and the fp32 sums
+// hold as precisely.
 constexpr float kLazyLog2 = 8.f;
 
 template <int D, int G, int R, int NK>
@@ -351,10 +359,15 @@ __device__ __forceinline__ void probs(const f32x4* sv, int g, float c, const flo
                                       float (&m)[G], float (&rs)[G], f32x4 (&o)[G][D / 16],
                                       float (&p)[NK]) {
     if (R != kOnline) {
+        if (scaled_route(R)) {
 #pragma unroll
-        for (int i = 0; i < NK; ++i)
-            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -shift[g]));
-        if (R == kFixedPmax) {
+            for (int i = 0; i < NK; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i >> 2][i & 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+                p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i >> 2][i & 3], c, -shift[g]));
+        }
+        if (pmax_route(R)) {
 #pragma unroll
             for (int i = 0; i < NK; ++i) m[g] = fmaxf(m[g], p[i]);
         }
@@ -439,15 +452,15 @@ struct NoHook {
 
 template <int D, int G, typename Hook = NoHook>
 __device__ __forceinline__ void qk_pv(const bf16x8 (&ka)[D / 32][2], const bf16x8 (&qf)[G][D / 32],
-                                      f32x4 (&sn)[2][G], const bf16x8 (&va)[D / 16],
-                                      const bf16x2 (&pk)[G][4], f32x4 (&o)[G][D / 16],
-                                      const Hook& hook = Hook()) {
+                                      const f32x4 (&s0)[G], f32x4 (&sn)[2][G],
+                                      const bf16x8 (&va)[D / 16], const bf16x2 (&pk)[G][4],
+                                      f32x4 (&o)[G][D / 16], const Hook& hook = Hook()) {
     using GG = Geo<D>;
     constexpr int DPK = GG::DB / GG::KS;                // P.V column blocks per k-step
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int g = 0; g < G; ++g) sn[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < G; ++g) sn[b][g] = s0[g];
 #pragma unroll
     for (int ks = 0; ks < GG::KS; ++ks) {
 #pragma unroll
@@ -516,7 +529,8 @@ __device__ __forceinline__ void prio_vector_end() { __builtin_amdgcn_s_setprio(0
 template <int D, int G, int R>
 __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                        const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
-                                       const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
+                                       const f32x4 (&s0)[G], const float (&shift)[G],
+                                       float c, f32x4 (&o)[G][D / 16],
                                        float (&rs)[G], float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     constexpr int SPC = kBK / 32;                       // 32-key steps per chunk
@@ -532,7 +546,7 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
     if (nchunks > 1) issue_chunk4<D>(smem_lds + GG::STAGE, sl, Kh, Vh, 1, wave, lane);
 
     f32x4 sv[2][G];
-    scores<D, G, 2>(smem, 0, qf, sv, la);
+    scores<D, G, 2>(smem, 0, qf, s0, sv, la);
     int st = 0;                                         // stage of chunk ch
     for (int ch = 0; ch + 1 < nchunks; ++ch) {
         const unsigned char* S0 = smem + st * GG::STAGE;
@@ -566,11 +580,11 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
                 const unsigned dst = smem_lds + (st ^ 1) * GG::STAGE;
                 constexpr int NI = GG::BLOCKS / 4;
                 static_assert(NI <= GG::KS, "one copy group per k-step");
-                qk_pv<D, G>(ka, qf, sv, va, pk, o, [&](int ks) {
+                qk_pv<D, G>(ka, qf, s0, sv, va, pk, o, [&](int ks) {
                     if (ks < NI) issue_group<D, 4>(dst, sl, Kh, Vh, ch + 2, wave, lane, ks);
                 });
             } else {
-                qk_pv<D, G>(ka, qf, sv, va, pk, o);
+                qk_pv<D, G>(ka, qf, s0, sv, va, pk, o);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -588,7 +602,7 @@ __device__ __forceinline__ void attend(unsigned char* smem, const Slice& sl, con
             bf16x8 ka[GG::KS][2];
             load_k<D>(S0, k0 + 32, ka, la);
             softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
-            qk_pv<D, G>(ka, qf, sv, va, pk, o);
+            qk_pv<D, G>(ka, qf, s0, sv, va, pk, o);
         } else {
             softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
             pv<D, G>(va, pk, o);
@@ -690,7 +704,8 @@ __device__ __forceinline__ void walk8_barrier(unsigned lds0, const Slice& sl, co
 template <int D, int G, int R>
 __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                         const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
-                                        const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
+                                        const f32x4 (&s0)[G], const float (&shift)[G],
+                                       float c, f32x4 (&o)[G][D / 16],
                                         float (&rs)[G], float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
@@ -702,7 +717,7 @@ __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, co
     walk8_prologue<D>(lds0, sl, Kh, Vh, nchunks, wave, lane);
 
     f32x4 sv[2][G];
-    scores<D, G, 2>(smem, 0, qf, sv, la);
+    scores<D, G, 2>(smem, 0, qf, s0, sv, la);
     for (int t = 0; t + 1 < nsteps; ++t) {
         const unsigned char* S0 = smem + ((t >> 1) & 3) * GG::STAGE;
         bf16x8 va[GG::DB];
@@ -716,7 +731,7 @@ __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, co
         softmax<D, G, R, 2>(sv, c, shift, m, rs, o, pk);
         prio_vector_end();
         __builtin_amdgcn_sched_barrier(0);
-        qk_pv<D, G>(ka, qf, sv, va, pk, o);
+        qk_pv<D, G>(ka, qf, s0, sv, va, pk, o);
         __builtin_amdgcn_sched_barrier(0);
     }
     // The last step: 32 keys, or the slice's lone last 16-key granule.
@@ -759,8 +774,9 @@ __device__ __forceinline__ void copy_only8(unsigned char* smem, const Slice& sl,
 template <int D, int G, int R>
 __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& sl,
                                              const __bf16* Kh, const __bf16* Vh,
-                                             const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
-                                             float c, f32x4 (&o)[G][D / 16], float (&rs)[G],
+                                             const bf16x8 (&qf)[G][D / 32], const f32x4 (&s0)[G],
+                                             const float (&shift)[G], float c,
+                                             f32x4 (&o)[G][D / 16], float (&rs)[G],
                                              float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
@@ -779,7 +795,7 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
             f32x4 sv[2][G];
 #pragma unroll
             for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-            scores<D, G, 1>(S0, 16 * wave, qf, sv, la);
+            scores<D, G, 1>(S0, 16 * wave, qf, s0, sv, la);
             bf16x2 pk[G][2];
             softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
             pv_half<D, G>(S0 + GG::TILE, 16 * wave, pk, o, la);
@@ -804,8 +820,9 @@ __device__ __forceinline__ void attend_split(unsigned char* smem, const Slice& s
 template <int D, int G, int R>
 __device__ __forceinline__ void attend_split8(unsigned char* smem, const Slice& sl,
                                               const __bf16* Kh, const __bf16* Vh,
-                                              const bf16x8 (&qf)[G][D / 32], const float (&shift)[G],
-                                              float c, f32x4 (&o)[G][D / 16], float (&rs)[G],
+                                              const bf16x8 (&qf)[G][D / 32], const f32x4 (&s0)[G],
+                                              const float (&shift)[G], float c,
+                                              f32x4 (&o)[G][D / 16], float (&rs)[G],
                                               float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
@@ -823,7 +840,7 @@ __device__ __forceinline__ void attend_split8(unsigned char* smem, const Slice& 
             f32x4 sv[2][G];
 #pragma unroll
             for (int g = 0; g < G; ++g) sv[1][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-            scores<D, G, 1>(S0, k0, qf, sv, la);
+            scores<D, G, 1>(S0, k0, qf, s0, sv, la);
             bf16x2 pk[G][2];
             softmax<D, G, R, 1>(sv, c, shift, m, rs, o, pk);
             pv_half<D, G>(S0 + GG::TILE, k0, pk, o, la);
@@ -905,6 +922,24 @@ __device__ __forceinline__ bool combine_split(unsigned char* smem, f32x4 (&o)[G]
     return true;
 }
 
+// The slice walk of route R for a workgroup of W waves (split: the walk of
+// a workgroup left with a single row unit).
+template <int D, int G, int W, int R>
+__device__ __forceinline__ void walk(bool split, unsigned char* smem, const Slice& sl,
+                                     const __bf16* Kh, const __bf16* Vh,
+                                     const bf16x8 (&qf)[G][D / 32], const f32x4 (&s0)[G],
+                                     const float (&shift)[G], float c, f32x4 (&o)[G][D / 16],
+                                     float (&rs)[G], float (&m)[G], int wave, int lane) {
+    if (split) {
+        if (W == 8) attend_split8<D, G, R>(smem, sl, Kh, Vh, qf, s0, shift, c, o, rs, m, wave, lane);
+        else attend_split<D, G, R>(smem, sl, Kh, Vh, qf, s0, shift, c, o, rs, m, wave, lane);
+    } else if (W == 8) {
+        attend8<D, G, R>(smem, sl, Kh, Vh, qf, s0, shift, c, o, rs, m, wave, lane);
+    } else {
+        attend<D, G, R>(smem, sl, Kh, Vh, qf, s0, shift, c, o, rs, m, wave, lane);
+    }
+}
+
 // LDS of a workgroup: the key ring (4 stages for 8 waves, 2 for 4 waves); a
 // split workgroup reuses it to combine its waves' partials.
 template <int D, int G, int W>
@@ -918,7 +953,8 @@ constexpr int fwd_lds_bytes() {
 // two 4-wave workgroups or one 8-wave workgroup per CU.
 template <int D, int G, int W, bool PMAX>
 __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
-    constexpr int RF = PMAX ? kFixedPmax : kFixed;      // this kernel's fixed route
+    constexpr int RF = kFixed | (PMAX ? kPmax : 0);      // this kernel's fixed routes
+    constexpr int RQ = kFixedScaled | (PMAX ? kPmax : 0);
     using GG = Geo<D>;
     static_assert(W == 4 || W == 8, "4 or 8 waves");
     static_assert(G * D <= 256, "a wave's accumulators and query fragments fit 256 registers");
@@ -1000,23 +1036,62 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
     float shift[G], rs[G];
     f32x4 o[G][GG::DB];
     const float rsl = p.rslice[size_t(bh) * p.F + f];
+    bool wide = false;                                   // some row's bound above the limit
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int row = f * T + 16 * min(unit * G + g, ngran - 1) + ln;
 #pragma unroll
         for (int ks = 0; ks < GG::KS; ++ks)
             qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
-        shift[g] = p.qnorm[size_t(bh) * p.N + row] * rsl;
+        shift[g] = p.qnorm[size_t(bh) * p.N + row] * rsl;     // ||q_i|| R_S
+        wide |= shift[g] * c > FSA_ELIG_BETA * kLog2e;
         rs[g] = 0.f;
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (fixed) {
-        // The fixed route scores K as given, so each row's shift is its bound
-        // on the centred scores plus q.mu (the row's whole offset from
-        // centring). The 4 lanes holding a row's columns add their partial
-        // dot products in the same pairing order, so all 4 get the same sum.
-        const float* muh = p.mu + size_t(bh) * D;
+    // The scaled fixed route (taken by a wave whose rows all have c ||q_i|| R_S
+    // within the eligibility threshold, which every fixed-eligible head and
+    // frame meets by construction): the query fragments carry c, rounded to
+    // bf16 once here, q'_i = bf16(c q_i), and the products start from minus
+    // the row's shift ||q'_i|| R_S + q'_i.mu, the Cauchy-Schwarz bound taken
+    // on q'_i itself. The score products then yield the exponents of exp2
+    // with no vector operation per score, and no probability exceeds 1. The
+    // route computes the fixed-max softmax of q'_i: the rounding moves each
+    // exponent by at most 2^-9 c ||q_i|| ||k_j - mu|| beside a part common to
+    // the row that cancels in the normalisation, which the threshold keeps
+    // within 0.09 in log2 units (about 0.005 for random directions). Other
+    // fixed waves (the row-block route's looser blocks) take the exact route:
+    // the shift c (||q_i|| R_S + q_i.mu) on the query as given.
+    // The 4 lanes holding a row's columns add their partial sums in the same
+    // pairing order, so all 4 get the same values.
+    const float* muh = p.mu + size_t(bh) * D;
+    const f32x4 zero[G] = {};
+    float m[G];
+    if (!fixed) {
+        walk<D, G, W, kOnline>(split, smem, sl, Kh, Vh, qf, zero, shift, c, o, rs, m, uwave, lane);
+    } else if (__builtin_amdgcn_ballot_w64(wide) == 0) {
+        f32x4 s0[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float ss = 0.f, qm = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < GG::KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const __bf16 x = __bf16(float(qf[g][ks][e]) * c);
+                    qf[g][ks][e] = x;
+                    ss = fmaf(float(x), float(x), ss);
+                    qm = fmaf(float(x), muh[32 * ks + 8 * lj + e], qm);
+                }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            qm += __shfl_xor(qm, 16, 64);
+            qm += __shfl_xor(qm, 32, 64);
+            const float z = -fmaf(sqrtf(ss), rsl, qm);
+            s0[g] = f32x4{z, z, z, z};
+        }
+        walk<D, G, W, RQ>(split, smem, sl, Kh, Vh, qf, s0, shift, c, o, rs, m, uwave, lane);
+    } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float qm = 0.f;
@@ -1027,32 +1102,9 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
                     qm = fmaf(float(qf[g][ks][e]), muh[32 * ks + 8 * lj + e], qm);
             qm += __shfl_xor(qm, 16, 64);
             qm += __shfl_xor(qm, 32, 64);
-            shift[g] += qm;
+            shift[g] = (shift[g] + qm) * c;
         }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) shift[g] *= c;
-
-    float m[G];
-    if (split) {
-        if (W == 8) {
-            if (fixed)
-                attend_split8<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-            else
-                attend_split8<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-        } else {
-            if (fixed)
-                attend_split<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-            else
-                attend_split<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-        }
-    } else if (W == 8) {
-        if (fixed) attend8<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-        else attend8<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-    } else if (fixed) {
-        attend<D, G, RF>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
-    } else {
-        attend<D, G, kOnline>(smem, sl, Kh, Vh, qf, shift, c, o, rs, m, uwave, lane);
+        walk<D, G, W, RF>(split, smem, sl, Kh, Vh, qf, zero, shift, c, o, rs, m, uwave, lane);
     }
     if (PMAX && fixed) {
         // the largest probability this wave formed (every lane holds p >= 0,

@@ -407,10 +407,13 @@ def test_negative_controls_fail_the_bar(row_block):
 def test_fixed_route_probability_is_at_most_one(row_block):
     """The fixed max bounds every logit of its row (Cauchy-Schwarz on the
     centred keys), so no probability the fixed route forms exceeds 1; with
-    FSA_MODE_RECORD_PMAX the kernel records the largest one. It must be at
+    FSA_MODE_RECORD_PMAX the kernel records the largest one. Every row of this
+    workload is within the eligibility threshold, so every wave takes the
+    scaled fixed route, which scores the query q' = bf16(c q) (c = scale *
+    log2 e in fp32) against the bound ||q'|| R_S + q'.mu. The record must be at
     most 1 + 2^-8 (fp32 rounding of the scores and the shift), equal the
-    oracle's max over rows of exp(max_j s_ij - B_i) to fp32 rounding, and the
-    recording must leave the output bit-identical."""
+    oracle's max over rows of 2^(max_j q'.(k_j - mu) - ||q'|| R_S) to fp32
+    rounding, and the recording must leave the output bit-identical."""
     cfg = CONFIGS["small"].with_(H=2)
     say("largest fixed-route probability", row_block)
     run = Run(cfg, row_block=row_block).bounds()
@@ -420,15 +423,19 @@ def test_fixed_route_probability_is_at_most_one(row_block):
     pmax = float(run.views()["pmax"][0])
     Q, K = to_f64(run.Q), to_f64(run.K)
     b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    assert b["stat"].max() <= fsa.FSA_ELIG_BETA     # every row on the scaled route
+    c32 = np.float32(np.float32(cfg.scale) * np.float32(np.log2(np.e)))
+    q32 = run.Q.detach().to("cpu", torch.float32)
+    qs = (q32 * torch.tensor(c32)).to(torch.bfloat16).to(torch.float64).numpy()
     want = 0.0
     for h in range(cfg.H):
         kc = K[0, h] - b["mu"][0, h]
         for f in range(cfg.F):
             keys = orc.slice_keys(cfg.F, cfg.T, cfg.window, cfg.ref_frame, f)
             rows = np.arange(f * cfg.T, (f + 1) * cfg.T)
-            s = cfg.scale * Q[0, h, rows] @ kc[keys].T
-            B = cfg.scale * b["qnorm"][0, h, rows] * b["R_S"][0, h, f]
-            want = max(want, float(np.exp(s.max(axis=1) - B).max()))
-    print(f"largest fixed-route p: {pmax:.6g} (oracle {want:.6g})")
+            s = qs[0, h, rows] @ kc[keys].T
+            B = np.linalg.norm(qs[0, h, rows], axis=1) * b["R_S"][0, h, f]
+            want = max(want, float(np.exp2(s.max(axis=1) - B).max()))
+    print(f"largest fixed-route p: {pmax:.6g} (oracle on q' {want:.6g})")
     assert 0.0 < pmax <= 1.0 + 2.0 ** -8
     assert pmax == pytest.approx(want, rel=2e-3)
