@@ -1044,24 +1044,22 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
         for (int ks = 0; ks < GG::KS; ++ks)
             qf[g][ks] = *reinterpret_cast<const bf16x8*>(Qh + size_t(row) * D + 32 * ks + 8 * lj);
         shift[g] = p.qnorm[size_t(bh) * p.N + row] * rsl;     // ||q_i|| R_S
-        wide |= shift[g] * c > FSA_ELIG_BETA * kLog2e;
+        wide |= shift[g] * c > FSA_SCALED_LIMIT;
         rs[g] = 0.f;
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // The scaled fixed route (taken by a wave whose rows all have c ||q_i|| R_S
-    // within the eligibility threshold, which every fixed-eligible head and
-    // frame meets by construction): the query fragments carry c, rounded to
-    // bf16 once here, q'_i = bf16(c q_i), and the products start from minus
-    // the row's shift ||q'_i|| R_S + q'_i.mu, the Cauchy-Schwarz bound taken
-    // on q'_i itself. The score products then yield the exponents of exp2
-    // with no vector operation per score, and no probability exceeds 1. The
-    // route computes the fixed-max softmax of q'_i: the rounding moves each
-    // exponent by at most 2^-9 c ||q_i|| ||k_j - mu|| beside a part common to
-    // the row that cancels in the normalisation, which the threshold keeps
-    // within 0.09 in log2 units (about 0.005 for random directions). Other
-    // fixed waves (the row-block route's looser blocks) take the exact route:
-    // the shift c (||q_i|| R_S + q_i.mu) on the query as given.
+    // within FSA_SCALED_LIMIT): the query fragments carry c, rounded to bf16
+    // once here, q'_i = bf16(c q_i), and the products start from minus the
+    // row's shift ||q'_i|| R_S + q'_i.mu, the Cauchy-Schwarz bound taken on
+    // q'_i itself. The score products then yield the exponents of exp2 with no
+    // vector operation per score, and no probability exceeds 1. The route
+    // computes the fixed-max softmax of q'_i: the rounding moves each exponent
+    // by at most 2^-9 c ||q_i|| ||k_j - mu|| <= 2^-4 beside a part common to
+    // the row that cancels in the normalisation. Other fixed waves (rows with
+    // keys spread wider) take the exact route: the shift
+    // c (||q_i|| R_S + q_i.mu) on the query as given, applied per score.
     // The 4 lanes holding a row's columns add their partial sums in the same
     // pairing order, so all 4 get the same values.
     const float* muh = p.mu + size_t(bh) * D;

@@ -44,6 +44,7 @@ MODES = {"auto": FSA_MODE_AUTO, "online": FSA_MODE_ONLINE_ONLY, "fixed": FSA_MOD
 
 FSA_ELIG_BETA = 32.0
 FSA_GAP_LIMIT = 64.0
+FSA_SCALED_LIMIT = 32.0
 FSA_MAX_FRAMES = 255
 FSA_STATIC_WS_BYTES = 16 << 20
 

@@ -103,6 +103,14 @@ typedef enum {
    FSA_ELIG_BETA, the largest gap between the fixed max and a row's true max
    that the per-head check allows (the logits of a row lie within +-B_i). */
 #define FSA_GAP_LIMIT 64.0f
+/* Limit, in log2 units, on c ||q_i|| R_S(f) (c = scale * log2 e) for the
+   forward's scaled fixed route: a wave of the fixed route whose rows all stay
+   within it scores q'_i = bf16(c q_i) against the bound taken on q'_i (one
+   exp per probability, no vector arithmetic before it); rounding c q_i moves
+   each exponent by at most 2^-9 times this, 2^-4, beyond a part common to the
+   row that cancels. Other fixed waves apply the scale per score, exactly.
+   ("Unchaining the Softmax" para. 2: the fixed max from precomputed norms.) */
+#define FSA_SCALED_LIMIT 32.0f
 /* Largest frame count a plan accepts. */
 #define FSA_MAX_FRAMES 255
 

@@ -24,6 +24,16 @@ def test_library_exports_every_declared_symbol():
     assert sorted(fsa.EXPORTS) == names
 
 
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    for name in ("FSA_ELIG_BETA", "FSA_GAP_LIMIT", "FSA_SCALED_LIMIT", "FSA_MAX_FRAMES"):
+        m = re.search(r"#define\s+%s\s+([0-9.]+)f?\b" % name, text)
+        assert m, name
+        assert float(getattr(fsa, name)) == float(m.group(1)), name
+    m = re.search(r"#define\s+FSA_STATIC_WS_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and fsa.FSA_STATIC_WS_BYTES == int(m.group(1)) << int(m.group(2))
+
+
 def test_status_strings():
     assert fsa.fsa_status_string(0) == "FSA_OK"
     assert fsa.fsa_status_string(-3) == "FSA_ERR_WORKSPACE"

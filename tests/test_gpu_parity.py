@@ -408,7 +408,7 @@ def test_fixed_route_probability_is_at_most_one(row_block):
     """The fixed max bounds every logit of its row (Cauchy-Schwarz on the
     centred keys), so no probability the fixed route forms exceeds 1; with
     FSA_MODE_RECORD_PMAX the kernel records the largest one. Every row of this
-    workload is within the eligibility threshold, so every wave takes the
+    workload has c ||q|| R_S within FSA_SCALED_LIMIT, so every wave takes the
     scaled fixed route, which scores the query q' = bf16(c q) (c = scale *
     log2 e in fp32) against the bound ||q'|| R_S + q'.mu. The record must be at
     most 1 + 2^-8 (fp32 rounding of the scores and the shift), equal the
@@ -423,8 +423,9 @@ def test_fixed_route_probability_is_at_most_one(row_block):
     pmax = float(run.views()["pmax"][0])
     Q, K = to_f64(run.Q), to_f64(run.K)
     b = orc.bounds(Q, K, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
-    assert b["stat"].max() <= fsa.FSA_ELIG_BETA     # every row on the scaled route
     c32 = np.float32(np.float32(cfg.scale) * np.float32(np.log2(np.e)))
+    rs = np.repeat(b["R_S"][0], cfg.T, axis=1)                  # [H][N]: R_S of each row
+    assert (c32 * b["qnorm"][0] * rs).max() <= 0.9 * fsa.FSA_SCALED_LIMIT   # every wave scaled
     q32 = run.Q.detach().to("cpu", torch.float32)
     qs = (q32 * torch.tensor(c32)).to(torch.bfloat16).to(torch.float64).numpy()
     want = 0.0
