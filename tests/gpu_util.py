@@ -30,6 +30,7 @@ REGRESSION = {
     "1080p": (7e-4, 8e-5, 5e-3),
     "stress": (2e-2, 4.5e-4, 4e-3),
     "720p-dense": (6e-4, 6e-5, 5e-3),
+    "small-wide": (1.1e-2, 4e-4, 5e-3),     # small, keys spread 1.42x wider (measured 2.8e-3)
 }
 
 

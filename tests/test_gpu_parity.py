@@ -352,6 +352,42 @@ def test_attention_entry_point():
 
 
 @pytest.mark.parametrize("row_block", ROW_BLOCKS)
+def test_scaled_and_exact_fixed_routes_in_one_launch(row_block):
+    """The small workload's keys spread 1.42x wider about their mean: every head
+    stays eligible, but the rows' c ||q|| R_S straddle FSA_SCALED_LIMIT, so
+    within one launch some waves of the fixed route take the scaled route and
+    the others the exact one (about 45% of the 32-row units are past the limit,
+    by the oracle's bounds). Every row meets the bar against the oracle, the
+    errors stay in the small workload's band, and no probability either route
+    forms exceeds 1 + 2^-8. The wider keys give peakier rows and larger
+    outputs, so the error band is this input's own (4x its measured error)."""
+    cfg = CONFIGS["small"].with_(H=4)
+    say("scaled and exact fixed routes", row_block)
+    base = Run(cfg)
+    Q, K, V = base.Q, base.K, base.V
+    Kf = K.float()
+    mu = Kf.mean(dim=2, keepdim=True)
+    K = (mu + 1.42 * (Kf - mu)).to(K.dtype)
+    Qd, Kd, Vd = (to_f64(t) for t in (Q, K, V))
+    b = orc.bounds(Qd, Kd, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    assert b["elig"].all()
+    c32 = np.float32(np.float32(cfg.scale) * np.float32(np.log2(np.e)))
+    x = (c32 * b["qnorm"][0] * np.repeat(b["R_S"][0], cfg.T, axis=1)).reshape(cfg.H, cfg.F, cfg.T)
+    units = [x[:, :, u:u + 32].max(-1) for u in range(0, cfg.T, 32)]
+    past = float(np.mean(np.stack(units) > fsa.FSA_SCALED_LIMIT))
+    assert 0.2 < past < 0.8, past
+    run = Run(cfg, inputs=(Q, K, V), row_block=row_block).bounds()
+    O = run.forward("auto")
+    want = orc.attention(Qd, Kd, Vd, cfg.F, cfg.T, cfg.window, cfg.ref_frame, cfg.scale)
+    assert_close(cfg, O, want, "mixed fixed routes")
+    assert_regression("small-wide", O, want, f"mixed fixed routes {row_block} ({past:.0%} of units exact)")
+    O_rec = run.forward(fsa.FSA_MODE_AUTO | fsa.FSA_MODE_RECORD_PMAX)
+    assert torch.equal(O, O_rec)
+    pmax = float(run.views()["pmax"][0])
+    assert 0.0 < pmax <= 1.0 + 2.0 ** -8
+
+
+@pytest.mark.parametrize("row_block", ROW_BLOCKS)
 def test_split_workgroups_exact_and_deterministic(row_block):
     """T = 3600 leaves each frame's last workgroup a single row unit (in
     128-row and in 256-row workgroups), which its waves split over the key
