@@ -22,20 +22,24 @@
 //    shorter (16, 32 or 48 keys, a whole number of 16-key granules, so still
 //    no partial block).
 //  * Two workgroup geometries, chosen per shape by the plan:
-//    - 8 waves (256 rows), one workgroup per CU: K and V chunks stream into a
-//      4-stage LDS ring by direct-to-LDS copies, shared by all 8 waves, with
-//      one barrier per pair of chunks; the copies of the pair after next are
-//      issued right after each barrier;
-//    - 4 waves (128 rows), two workgroups per CU: a 2-stage ring with one
-//      barrier per chunk (used where a frame's rows fill 256-row workgroups
-//      poorly, and for the split walk of a frame's last single unit).
-//    In both, the V^T operand of P.V is read transposed out of row-major V
-//    (ds_read_b64_tr_b16), and two waves share each SIMD so that one wave's
-//    softmax runs while the other's products occupy the matrix unit.
-//  * Both routes score K as given. The fixed route's shift for row i is its
+//    - 4 waves (128 rows), two workgroups per CU, most shapes: K and V chunks
+//      stream into a 2-stage LDS ring by direct-to-LDS copies, shared by the 4
+//      waves, with one barrier per chunk;
+//    - 8 waves (256 rows), one workgroup per CU, where large frames fill
+//      256-row workgroups to within one row unit: a 4-stage ring with one
+//      barrier per pair of chunks, each chunk copied once for twice the rows;
+//      the copies of the pair after next are issued right after each barrier.
+//    In both, a frame's last workgroup, when left with a single row unit,
+//    splits the key chunks among its waves instead (attend_split,
+//    attend_split8); the V^T operand of P.V is read transposed out of
+//    row-major V (ds_read_b64_tr_b16), and two waves share each SIMD.
+//  * Every route scores K as given. The fixed route's shift for row i is its
 //    bound on the centred scores, scale ||q_i|| R_S, plus scale q_i.mu:
 //    centring moves every score of the row by that amount, so the softmax is
-//    the same and no centred copy of K is ever stored.
+//    the same and no centred copy of K is ever stored. A fixed wave whose rows
+//    keep c ||q_i|| R_S within FSA_SCALED_LIMIT takes the scaled fixed route:
+//    the scale rides in its query fragments and the shift is the products'
+//    starting value, so each probability is a single exp2 of a product.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: the accumulator then holds, per lane, one query
 //    and 4+4 keys, which is exactly the B-operand layout of O^T = V^T P^T, so P
