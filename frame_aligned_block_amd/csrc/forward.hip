@@ -709,7 +709,7 @@ template <int D, int G, int R>
 __device__ __forceinline__ void attend8(unsigned char* smem, const Slice& sl, const __bf16* Kh,
                                         const __bf16* Vh, const bf16x8 (&qf)[G][D / 32],
                                         const f32x4 (&s0)[G], const float (&shift)[G],
-                                       float c, f32x4 (&o)[G][D / 16],
+                                        float c, f32x4 (&o)[G][D / 16],
                                         float (&rs)[G], float (&m)[G], int wave, int lane) {
     using GG = Geo<D>;
     const LaneAddr la = lane_addr(lane & 15, lane >> 4);
