@@ -425,6 +425,12 @@ __device__ __forceinline__ void softmax(const f32x4 (&s)[2][G], float c, const f
         for (int i = 0; i < 2 * NB; ++i) pk[g][i] = bf16x2{__bf16(p[2 * i]), __bf16(p[2 * i + 1])};
         rs[g] = sum_pairs(pk[g], 2 * NB, rs[g]);
     }
+    // Keep the row sums in this step: the compiler otherwise sinks some of the
+    // additions past the next barrier and its copy branch, where the packed
+    // pairs are gone, and packs those pairs a second time (4 conversions and
+    // 2 permutes per 64 keys; 1.6% of the 720p forward).
+#pragma unroll
+    for (int g = 0; g < G; ++g) asm volatile("" :: "v"(rs[g]));
 }
 
 // K operands of the 32 keys at koff: 16 rows per 16-key block, all D/32
