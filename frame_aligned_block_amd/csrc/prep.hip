@@ -94,35 +94,55 @@ __device__ __forceinline__ void lds_copy16(unsigned lds, const void* gbase, unsi
                  :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Copy i (0 <= i < kCopiesPerChunk) of wave `wave`'s share of input channel
-// chunk kc. The chunk is kRows/16 blocks of W' (the workgroup's output
-// channels; rows past the last head repeat it, never stored), then kTok/16
-// blocks of X (rows past the last token repeat it, never stored), each 16
-// rows x 64 bytes; wave w takes blocks j = kPrepWaves * i + w. The 16-byte
-// segment is swizzled by (row >> 1) & 3.
-__device__ __forceinline__ void issue_copy(unsigned stage, const unsigned char* Wrows, int nwrows,
-                                           const unsigned char* Xrows, int ntok, int C, int kc,
-                                           int wave, int lane, int i) {
+// The copies of a wave's share of input channel chunk kc. The chunk is
+// kRows/16 blocks of W' (the workgroup's output channels; rows past the last
+// head repeat it, never stored), then kTok/16 blocks of X (rows past the last
+// token repeat it, never stored), each 16 rows x 64 bytes; wave w takes blocks
+// j = kPrepWaves * i + w, so copies 0-1 are blocks of W' and 2-3 of X. The
+// 16-byte segment is swizzled by (row >> 1) & 3. Each lane's global offset
+// and LDS offset are the same for every chunk (CopyPlan, computed once); the
+// chunk's offset of kc * 64 bytes is uniform and rides on the scalar base, so
+// issuing a copy takes no vector instruction.
+struct CopyPlan {
+    unsigned voff[kCopiesPerChunk];
+    unsigned lds[kCopiesPerChunk];
+};
+static_assert(kRows / 16 == 2 * kPrepWaves && kTok / 16 == 2 * kPrepWaves && kCopiesPerChunk == 4,
+              "copies 0-1 of W', 2-3 of X");
+
+__device__ __forceinline__ CopyPlan copy_plan(int nwrows, int ntok, int C, int wave, int lane) {
+    CopyPlan cp;
     const int seg = lane & 3, rr = lane >> 2;
-    const unsigned col = unsigned(kc * kKC) * 2 + 16 * (seg ^ ((lane >> 3) & 3));
-    const int j = kPrepWaves * i + wave;
-    if (j < kRows / 16) {
-        const int wrow = min(16 * j + rr, nwrows - 1);
-        lds_copy16(stage + j * 1024, Wrows, unsigned(wrow) * unsigned(C) * 2 + col);
-    } else {
-        const int rb = j - kRows / 16;
-        const int xrow = min(16 * rb + rr, ntok - 1);
-        lds_copy16(stage + kWSub + rb * 1024, Xrows, unsigned(xrow) * unsigned(C) * 2 + col);
+    const unsigned col = 16 * (seg ^ ((lane >> 3) & 3));
+#pragma unroll
+    for (int i = 0; i < kCopiesPerChunk; ++i) {
+        const int j = kPrepWaves * i + wave;
+        if (i < 2) {
+            const int wrow = min(16 * j + rr, nwrows - 1);
+            cp.voff[i] = unsigned(wrow) * unsigned(C) * 2 + col;
+            cp.lds[i] = j * 1024;
+        } else {
+            const int rb = j - kRows / 16;
+            const int xrow = min(16 * rb + rr, ntok - 1);
+            cp.voff[i] = unsigned(xrow) * unsigned(C) * 2 + col;
+            cp.lds[i] = kWSub + rb * 1024;
+        }
     }
+    return cp;
+}
+
+__device__ __forceinline__ void issue_copy(unsigned stage, const unsigned char* Wrows,
+                                           const unsigned char* Xrows, int kc, const CopyPlan& cp,
+                                           int i) {
+    const unsigned char* base = (i < 2 ? Wrows : Xrows) + size_t(kc) * (kKC * 2);
+    lds_copy16(stage + cp.lds[i], base, cp.voff[i]);
 }
 
 // All of a wave's copies of chunk kc.
-__device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows, int nwrows,
-                                            const unsigned char* Xrows, int ntok, int C, int kc,
-                                            int wave, int lane) {
+__device__ __forceinline__ void issue_chunk(unsigned stage, const unsigned char* Wrows,
+                                            const unsigned char* Xrows, int kc, const CopyPlan& cp) {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerChunk; ++i)
-        issue_copy(stage, Wrows, nwrows, Xrows, ntok, C, kc, wave, lane, i);
+    for (int i = 0; i < kCopiesPerChunk; ++i) issue_copy(stage, Wrows, Xrows, kc, cp, i);
 }
 
 // Operand i of this wave for one chunk, one 16-byte read per lane: i < G are
@@ -219,9 +239,10 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
         for (int cb = 0; cb < NB; ++cb) acc[g][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ka = ln * 64 + 16 * (lj ^ ((ln >> 1) & 3));    // this lane's 16 bytes of a 16-row block
+    const CopyPlan cp = copy_plan(nwrows, ntok, p.C, uwave, lane);
     // Chunk c lives in stage c % kStages. The ring starts full.
     for (int c = 0; c < kStages && c < nchunks; ++c)
-        issue_chunk(smem_lds + c * kStage, Wrows, nwrows, Xrows, ntok, p.C, c, uwave, lane);
+        issue_chunk(smem_lds + c * kStage, Wrows, Xrows, c, cp);
     wait_chunk(min(kStages, nchunks) - 1);               // chunk 0 has landed
     __builtin_amdgcn_s_barrier();
     bf16x8 xb[2][G], wa[2][NB];
@@ -256,7 +277,7 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
                     load_operand<G, NB>(next, wr, wc, ka, i, xb[u ^ 1], wa[u ^ 1]);
             }
             if (copies && cb < kCopiesPerChunk)
-                issue_copy(stage, Wrows, nwrows, Xrows, ntok, p.C, k + kStages, uwave, lane, cb);
+                issue_copy(stage, Wrows, Xrows, k + kStages, cp, cb);
         });
     };
     // Steady trips have no branch inside: chunk k+1 exists, chunks k+2 and
