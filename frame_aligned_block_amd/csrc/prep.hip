@@ -46,6 +46,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr int kPrepWaves = 8;             // waves of a workgroup: two per SIMD, one workgroup per CU
 constexpr int kTG = 64;                   // tokens per wave (4 granules of 16)
@@ -296,6 +298,15 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
     PREP_WAIT_VMCNT0();
 
     // ---- epilogue: row scale, rotation, rounding, statistics, store
+    // Each wave stages its 64 x 128 bf16 output tile in its own 16 KB of the
+    // ring (free once every wave has passed the barrier below) and stores it
+    // back as whole 256-byte rows, 16 bytes a lane: half the store
+    // instructions of storing each lane's 4 channels, and whole cache lines.
+    // The 16-byte segment of row r sits at segment ^ (r & 15), which keeps
+    // both the staging writes and the row reads on distinct banks.
+    static_assert(kPrepWaves * kTG * kCh * 2 <= kStages * kStage, "staging fits the ring");
+    __syncthreads();                                     // no wave reads the ring any more
+    const unsigned stage_out = smem_lds + uwave * (kTG * kCh * 2);
     const bool rotate = part < 2;
     __bf16* out = static_cast<__bf16*>(part == 0 ? p.Q : part == 1 ? p.K : p.V) +
                   (size_t(b) * p.H + h) * p.N * D;
@@ -341,12 +352,26 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
 #pragma unroll
                 for (int e = 0; e < 4; ++e) csum[cb][e] += float(o4[e]);
             }
-            if (live) *reinterpret_cast<bf16x4*>(out + size_t(n) * D + 16 * cb + 4 * lj) = o4;
+            {
+                const int r = 16 * g + ln;                   // row of the wave's tile
+                const unsigned seg = unsigned(2 * cb + (lj >> 1)) ^ unsigned(r & 15);
+                *(lds_bf16x4*)(stage_out + r * (kCh * 2) + seg * 16 + (lj & 1) * 8) = o4;
+            }
         }
         if (part == 0) {
             qq += __shfl_xor(qq, 16, 64);
             qq += __shfl_xor(qq, 32, 64);
             if (live && lj == 0) p.qnorm[(size_t(b) * p.H + h) * p.N + n] = sqrtf(qq);
+        }
+    }
+    // the staged tile, 4 rows per read: lane l takes row 4i + l/16, segment l%16
+    if (col_live) {
+#pragma unroll
+        for (int i = 0; i < kTG / 4; ++i) {
+            const int r = 4 * i + (lane >> 4), sg = lane & 15;
+            const int tl = kTG * wr + r;
+            const bf16x8 v = *(const lds_bf16x8*)(stage_out + r * (kCh * 2) + ((sg ^ (r & 15)) * 16));
+            if (tl < ntok) *reinterpret_cast<bf16x8*>(out + size_t(tok0 + tl) * D + 8 * sg) = v;
         }
     }
     // key column sums: over the 16 tokens of each lane group, then the 2 wave
