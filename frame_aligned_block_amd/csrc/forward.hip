@@ -177,6 +177,7 @@ constexpr int kBK = 64;                 // keys per LDS chunk
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // LDS tiles. A chunk's K (and V) tile is D/32 column sub-tiles of 64 rows x
@@ -1124,22 +1125,61 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
         for (int off = 1; off < 64; off <<= 1) pm = fmaxf(pm, __shfl_xor(pm, off, 64));
         if (lane == 0 && pm > 0.f) atomicMax(p.pmax, __float_as_uint(pm));
     }
-    if (split && !combine_split<D, G, W>(smem, o, rs, m, c, fixed, uwave, lane)) return;
-
+    // (the kernels that record the fixed route's largest probability, a check
+    // run in tests, keep direct stores: staging would spill their registers)
+    if (split || PMAX) {
+        if (split && !combine_split<D, G, W>(smem, o, rs, m, c, fixed, uwave, lane)) return;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g >= nvalid) break;
+            float tot = rs[g] + __shfl_xor(rs[g], 16, 64);
+            tot += __shfl_xor(tot, 32, 64);
+            const float inv = 1.0f / tot;
+            const int row = f * T + 16 * (unit * G + g) + ln;
+#pragma unroll
+            for (int db = 0; db < GG::DB; ++db) {
+                bf16x4 out;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[i] = __bf16(o[g][db][i] * inv);
+                *reinterpret_cast<bf16x4*>(Oh + size_t(row) * D + 16 * db + 4 * lj) = out;
+            }
+        }
+        return;
+    }
+    // The wave's 16G x D output tile goes through its own 2*16G*D bytes of the
+    // key ring (free once every computing wave has passed the barrier below;
+    // the waves that only stage keys have returned), then out as whole rows,
+    // 16 bytes a lane: half the store instructions, whole cache lines. The
+    // 16-byte segment of row r sits at segment ^ (r & 15), so both the writes
+    // and the row reads stay on distinct banks.
+    constexpr int RB2 = D * 2;                           // bytes per row
+    constexpr int SPR = RB2 / 16;                        // 16-byte segments per row
+    static_assert(W * 16 * G * RB2 <= fwd_lds_bytes<D, G, W>(), "staging fits the ring");
+    const unsigned stage_out = unsigned(uintptr_t((lds_void*)smem)) + uwave * (16 * G * RB2);
+    FSA_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        if (g >= nvalid) break;
         float tot = rs[g] + __shfl_xor(rs[g], 16, 64);
         tot += __shfl_xor(tot, 32, 64);
         const float inv = 1.0f / tot;
-        const int row = f * T + 16 * (unit * G + g) + ln;
+        const int r = 16 * g + ln;
 #pragma unroll
         for (int db = 0; db < GG::DB; ++db) {
             bf16x4 out;
 #pragma unroll
             for (int i = 0; i < 4; ++i) out[i] = __bf16(o[g][db][i] * inv);
-            *reinterpret_cast<bf16x4*>(Oh + size_t(row) * D + 16 * db + 4 * lj) = out;
+            const unsigned seg = unsigned(2 * db + (lj >> 1)) ^ unsigned(r & (SPR - 1) & 15);
+            *(lds_bf16x4*)(stage_out + r * RB2 + seg * 16 + (lj & 1) * 8) = out;
         }
+    }
+    constexpr int RPR = 64 / SPR;                        // rows per read
+#pragma unroll
+    for (int i = 0; i < 16 * G / RPR; ++i) {
+        const int r = RPR * i + lane / SPR, sg = lane % SPR;
+        const bf16x8 v = *(const lds_bf16x8*)(stage_out + r * RB2 + ((sg ^ (r & (SPR - 1) & 15)) * 16));
+        if (r < 16 * nvalid)
+            *reinterpret_cast<bf16x8*>(Oh + size_t(f * T + 16 * unit * G + r) * D + 8 * sg) = v;
     }
 }
 
