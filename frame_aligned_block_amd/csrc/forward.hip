@@ -1149,9 +1149,10 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
     // The wave's 16G x D output tile goes through its own 2*16G*D bytes of the
     // key ring (free once every computing wave has passed the barrier below;
     // the waves that only stage keys have returned), then out as whole rows,
-    // 16 bytes a lane: half the store instructions, whole cache lines. The
-    // 16-byte segment of row r sits at segment ^ (r & 15), so both the writes
-    // and the row reads stay on distinct banks.
+    // 16 bytes a lane: half the store instructions, whole cache lines. In row
+    // r, 16-byte segment s sits at s ^ (r & 7) and its two 8-byte halves trade
+    // places when r & 8, so that the 16 rows one write instruction touches
+    // fill 128 distinct bytes of banks and each row read takes whole lines.
     constexpr int RB2 = D * 2;                           // bytes per row
     constexpr int SPR = RB2 / 16;                        // 16-byte segments per row
     static_assert(W * 16 * G * RB2 <= fwd_lds_bytes<D, G, W>(), "staging fits the ring");
@@ -1169,15 +1170,17 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16(const FwdArgs p) {
             bf16x4 out;
 #pragma unroll
             for (int i = 0; i < 4; ++i) out[i] = __bf16(o[g][db][i] * inv);
-            const unsigned seg = unsigned(2 * db + (lj >> 1)) ^ unsigned(r & (SPR - 1) & 15);
-            *(lds_bf16x4*)(stage_out + r * RB2 + seg * 16 + (lj & 1) * 8) = out;
+            const unsigned seg = unsigned(2 * db + (lj >> 1)) ^ unsigned(r & 7);
+            const unsigned half = unsigned(lj & 1) ^ unsigned((r >> 3) & 1);
+            *(lds_bf16x4*)(stage_out + r * RB2 + seg * 16 + half * 8) = out;
         }
     }
     constexpr int RPR = 64 / SPR;                        // rows per read
 #pragma unroll
     for (int i = 0; i < 16 * G / RPR; ++i) {
         const int r = RPR * i + lane / SPR, sg = lane % SPR;
-        const bf16x8 v = *(const lds_bf16x8*)(stage_out + r * RB2 + ((sg ^ (r & (SPR - 1) & 15)) * 16));
+        bf16x8 v = *(const lds_bf16x8*)(stage_out + r * RB2 + ((sg ^ (r & 7)) * 16));
+        if ((r >> 3) & 1) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
         if (r < 16 * nvalid)
             *reinterpret_cast<bf16x8*>(Oh + size_t(f * T + 16 * unit * G + r) * D + 8 * sg) = v;
     }

@@ -302,8 +302,10 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
     // ring (free once every wave has passed the barrier below) and stores it
     // back as whole 256-byte rows, 16 bytes a lane: half the store
     // instructions of storing each lane's 4 channels, and whole cache lines.
-    // The 16-byte segment of row r sits at segment ^ (r & 15), which keeps
-    // both the staging writes and the row reads on distinct banks.
+    // In row r, 16-byte segment s sits at s ^ (r & 7) and its two 8-byte
+    // halves trade places when r & 8, so that the 16 rows one write
+    // instruction touches fill 128 distinct bytes of banks and each row read
+    // takes whole lines.
     static_assert(kPrepWaves * kTG * kCh * 2 <= kStages * kStage, "staging fits the ring");
     __syncthreads();                                     // no wave reads the ring any more
     const unsigned stage_out = smem_lds + uwave * (kTG * kCh * 2);
@@ -354,8 +356,9 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
             }
             {
                 const int r = 16 * g + ln;                   // row of the wave's tile
-                const unsigned seg = unsigned(2 * cb + (lj >> 1)) ^ unsigned(r & 15);
-                *(lds_bf16x4*)(stage_out + r * (kCh * 2) + seg * 16 + (lj & 1) * 8) = o4;
+                const unsigned seg = unsigned(2 * cb + (lj >> 1)) ^ unsigned(r & 7);
+                const unsigned half = unsigned(lj & 1) ^ unsigned((r >> 3) & 1);
+                *(lds_bf16x4*)(stage_out + r * (kCh * 2) + seg * 16 + half * 8) = o4;
             }
         }
         if (part == 0) {
@@ -370,7 +373,8 @@ __global__ __launch_bounds__(kPrepWaves * 64, kPerCU) void prep_qkv(const PrepAr
         for (int i = 0; i < kTG / 4; ++i) {
             const int r = 4 * i + (lane >> 4), sg = lane & 15;
             const int tl = kTG * wr + r;
-            const bf16x8 v = *(const lds_bf16x8*)(stage_out + r * (kCh * 2) + ((sg ^ (r & 15)) * 16));
+            bf16x8 v = *(const lds_bf16x8*)(stage_out + r * (kCh * 2) + ((sg ^ (r & 7)) * 16));
+            if ((r >> 3) & 1) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
             if (tl < ntok) *reinterpret_cast<bf16x8*>(out + size_t(tok0 + tl) * D + 8 * sg) = v;
         }
     }
