@@ -2,7 +2,7 @@
 """Benchmark of frame-aligned windowed attention on one MI355X.
 
 One step is one pass of the whole hot path over one batch of synthetic input,
-already resident in HBM: fsa_bounds (key mean, centred keys, norms,
+already resident in HBM: fsa_bounds (key mean, key radii, query norms,
 eligibility) then fsa_forward (the attention), through the C ABI, on torch's
 current stream. The tile plan is built once per shape before timing.
 

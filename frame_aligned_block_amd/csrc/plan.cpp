@@ -48,9 +48,9 @@ constexpr int32_t kGranules = 2;
 //    to different workgroups and stay out of phase.
 // Same-process measurements: 8 waves 0.6-1.6% faster on the 1080p-shaped
 // chunk (T = 8160: 255 row units per frame, every 8-wave workgroup full but
-// the last, one unit short); even at 720p (T = 3600: 113 units, the last
-// workgroup of each frame left with one unit); 4 waves 18% faster on the
-// small chunk (T = 880) and 1% on the cross workload. So 8 waves where frames
+// the last, one unit short); 4 waves 1% faster at 720p (T = 3600: 113 units,
+// the last 8-wave workgroup of each frame left with one unit), 14% on the
+// small chunk (T = 880) and 4% on the cross workload. So 8 waves where frames
 // are large and fill 8-wave workgroups to within one unit, else 4.
 int32_t pick_waves(const fsa_shape& s) {
     const int32_t units = (s.T / 16 + kGranules - 1) / kGranules;

@@ -367,6 +367,16 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
+def _check_inputs(pairs, like, what: str) -> None:
+    """Each (tensor, shape) of pairs: a contiguous CUDA tensor of that shape,
+    with like's dtype, on like's device (the kernels take one device's
+    pointers)."""
+    for t, shp in pairs:
+        if not t.is_cuda or t.device != like.device or not t.is_contiguous() \
+                or tuple(t.shape) != tuple(shp) or t.dtype != like.dtype:
+            raise ValueError(what)
+
+
 def _check_out_ws(out, ws, like, need: int) -> None:
     """The C ABI cannot see buffer sizes: reject an output or workspace that
     the kernels would overrun or misread."""
@@ -393,20 +403,20 @@ def attention(q, k, v, F: int, T: int, window: int, ref_frame: int, scale: float
     B, H, N, d = q.shape
     if N != F * T:
         raise ValueError(f"N={N} != F*T={F * T}")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous CUDA tensors of one shape and dtype")
+    _check_inputs(((q, q.shape), (k, q.shape), (v, q.shape)), q,
+                  "q, k, v must be contiguous CUDA tensors of one shape, dtype and device")
     if scale is None:
         scale = d ** -0.5
     code = dtype_code(q)
     need = fsa_attention_workspace_bytes(F, T, window, ref_frame, B, H, d, code)
     _check_out_ws(out, ws, q, need)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    fsa_attention(q, k, v, out, F, T, window, ref_frame, scale, B, H, d, code, mode, ws,
-                  ws.numel() * ws.element_size())
+    with torch.cuda.device(q.device):           # launch on q's device and its current stream
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        fsa_attention(q, k, v, out, F, T, window, ref_frame, scale, B, H, d, code, mode, ws,
+                      ws.numel() * ws.element_size())
     return out
 
 
@@ -421,22 +431,21 @@ def cross_attention(q, kr, vr, F: int, T: int, scale: float | None = None, mode=
     M = kr.shape[2]
     if N != F * T:
         raise ValueError(f"N={N} != F*T={F * T}")
-    for t, shp in ((q, q.shape), (kr, (B, H, M, d)), (vr, (B, H, M, d))):
-        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shp) \
-                or t.dtype != q.dtype:
-            raise ValueError("q [B,H,F*T,d], kr and vr [B,H,M,d] must be contiguous CUDA "
-                             "tensors of one dtype")
+    _check_inputs(((q, q.shape), (kr, (B, H, M, d)), (vr, (B, H, M, d))), q,
+                  "q [B,H,F*T,d], kr and vr [B,H,M,d] must be contiguous CUDA tensors of "
+                  "one dtype and device")
     if scale is None:
         scale = d ** -0.5
     code = dtype_code(q)
     need = fsa_cross_attention_workspace_bytes(F, T, M, B, H, d, code)
     _check_out_ws(out, ws, q, need)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    fsa_cross_attention(q, kr, vr, out, F, T, M, scale, B, H, d, code, mode, ws,
-                        ws.numel() * ws.element_size())
+    with torch.cuda.device(q.device):           # launch on q's device and its current stream
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        fsa_cross_attention(q, kr, vr, out, F, T, M, scale, B, H, d, code, mode, ws,
+                            ws.numel() * ws.element_size())
     return out
 
 

@@ -285,6 +285,22 @@ def test_attention_rejects_bad_out_and_workspace():
     fsa._check_out_ws(None, None, q, 1024)                                 # nothing given
 
 
+def test_attention_rejects_bad_inputs():
+    """Inputs must be contiguous CUDA tensors of the stated shapes, one dtype
+    and one device; CPU tensors, a wrong shape, dtype or layout are rejected
+    before anything reaches the C ABI."""
+    import torch
+    q = torch.zeros(1, 2, 5 * 48, 64)
+    with pytest.raises(ValueError):
+        fsa._check_inputs(((q, q.shape),), q, "cpu")                        # not on a GPU
+    with pytest.raises(ValueError):
+        fsa.attention(q, q, q, F=5, T=48, window=1, ref_frame=0)           # through the wrapper
+    with pytest.raises(ValueError):
+        fsa.cross_attention(q, q[:, :, :48], q[:, :, :48], F=5, T=48)
+    with pytest.raises(ValueError):
+        fsa.attention(q, q, q, F=4, T=48, window=1, ref_frame=0)           # N != F*T
+
+
 def test_record_pmax_flag_validation():
     """FSA_MODE_RECORD_PMAX combines with any route of a bf16 plan; an fp32
     plan rejects it, and unknown mode bits are rejected, before any launch."""
