@@ -338,6 +338,9 @@ def main() -> int:
                     help="time the oracle on this many heads and scale (0: the whole call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bq", type=int, default=0)
+    ap.add_argument("--row-block", type=int, default=0,
+                    help="rows per workgroup of the bf16 forward (128: 4 waves, 256: 8 waves; "
+                         "0: the plan's choice)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     ap.add_argument("--extra", default="stress,1080p",
                     help="other workloads whose forward is timed after the 720p line's "
@@ -373,6 +376,8 @@ def main() -> int:
     else:
         plan = fsa.fsa_plan_create(fsa.make_shape(cfg.B, cfg.H, cfg.F, cfg.T, cfg.d,
                                                   cfg.window, cfg.ref_frame, args.bq, 0, code))
+    if args.row_block:
+        fsa.fsa_plan_set_row_block(plan, args.row_block)
     ws = torch.zeros(fsa.fsa_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
     O = torch.empty_like(Q)
     pairs = fsa.fsa_plan_valid_pairs(plan)

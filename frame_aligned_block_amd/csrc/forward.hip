@@ -21,14 +21,14 @@
 //    as one sequence in chunks of 64 keys; only the very last chunk can be
 //    shorter (16, 32 or 48 keys, a whole number of 16-key granules, so still
 //    no partial block).
-//  * Two workgroup geometries, chosen per shape by the plan:
-//    - 4 waves (128 rows), two workgroups per CU, most shapes: K and V chunks
-//      stream into a 2-stage LDS ring by direct-to-LDS copies, shared by the 4
-//      waves, with one barrier per chunk;
-//    - 8 waves (256 rows), one workgroup per CU, where large frames fill
-//      256-row workgroups to within one row unit: a 4-stage ring with one
-//      barrier per pair of chunks, each chunk copied once for twice the rows;
-//      the copies of the pair after next are issued right after each barrier.
+//  * Two workgroup geometries, recorded in the plan:
+//    - 4 waves (128 rows), two workgroups per CU, the plan's choice: K and V
+//      chunks stream into a 2-stage LDS ring by direct-to-LDS copies, shared
+//      by the 4 waves, with one barrier per chunk;
+//    - 8 waves (256 rows), one workgroup per CU, on request: a 4-stage ring
+//      with one barrier per pair of chunks, each chunk copied once for twice
+//      the rows; the copies of the pair after next are issued right after
+//      each barrier.
 //    In both, a frame's last workgroup, when left with a single row unit,
 //    splits the key chunks among its waves instead (attend_split,
 //    attend_split8); the V^T operand of P.V is read transposed out of

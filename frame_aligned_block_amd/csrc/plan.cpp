@@ -37,27 +37,21 @@ int32_t pick_bq(int32_t T) {
 // d = 128; d = 64 keeps the same 32 rows per wave.
 constexpr int32_t kGranules = 2;
 
-// Waves per workgroup of the bf16 forward kernel, per shape ("Unchaining the
-// Softmax" ¶3 re-tunes block shapes together with the softmax).
-//  * 8-wave workgroups (256 rows, one per CU) stage each key chunk once for
-//    twice the rows, so the CU moves half the bytes from L2 into LDS and
-//    holds a higher clock under the chip's power limit (1.93 against 1.76
-//    GHz at 720p); but their barriers line up the two waves of every SIMD,
-//    which costs about as many cycles as the clock gains.
+// Waves per workgroup of the bf16 forward kernel ("Unchaining the Softmax" ¶3
+// re-tunes block shapes together with the softmax). Two geometries exist:
 //  * 4-wave workgroups (128 rows, two per CU): the two waves of a SIMD belong
 //    to different workgroups and stay out of phase.
-// Same-process measurements: 8 waves 0.6-1.6% faster on the 1080p-shaped
-// chunk (T = 8160: 255 row units per frame, every 8-wave workgroup full but
-// the last, one unit short); 4 waves 1% faster at 720p (T = 3600: 113 units,
-// the last 8-wave workgroup of each frame left with one unit), 14% on the
-// small chunk (T = 880) and 4% on the cross workload. So 8 waves where frames
-// are large and fill 8-wave workgroups to within one unit, else 4.
-int32_t pick_waves(const fsa_shape& s) {
-    const int32_t units = (s.T / 16 + kGranules - 1) / kGranules;
-    const bool large = units >= 128;                     // 16 or more 8-wave workgroups
-    const bool fills = units % 8 == 0 || units % 8 == 7;
-    return large && fills ? 8 : 4;
-}
+//  * 8-wave workgroups (256 rows, one per CU) stage each key chunk once for
+//    twice the rows, so the CU moves half the bytes from L2 into LDS and
+//    holds a higher clock under the chip's power limit; but their barriers
+//    line up the two waves of every SIMD, which costs more cycles than the
+//    clock gains.
+// Same-process measurements of this kernel, 4 waves against 8: 3% faster at
+// 720p, 1.0-1.6% at 1080p (T = 8160, where every 8-wave workgroup but a
+// frame's last is full), 1% on stress, 4% on the cross workload, 15% on the
+// small chunk, equal on the dense one. So every shape takes 4 waves, and
+// fsa_plan_set_row_block selects 8.
+int32_t pick_waves(const fsa_shape&) { return 4; }
 
 // k-block size of the tile list when the caller leaves it open: as pick_bq,
 // over the key frame's span.

@@ -20,8 +20,8 @@ from gpu_util import (BF16_MAX_ABS, BF16_MEAN_ABS, Run, assert_close, assert_reg
 pytestmark = pytest.mark.gpu
 
 # Workgroup geometries of the bf16 forward kernel: 4 waves (128 rows, the
-# plan's choice for most shapes) and 8 waves (256 rows, its choice at 1080p);
-# every workload runs on both.
+# plan's choice) and 8 waves (256 rows, on request); every workload runs on
+# both.
 ROW_BLOCKS = (128, 256)
 
 if not torch.cuda.is_available():   # collected on CPU too; every test here is gpu-marked
@@ -119,7 +119,8 @@ def test_small_bf16_full(row_block):
 
 @pytest.mark.parametrize("name,heads,row_block", [
     ("720p", [0, 11, 23], 0), ("1080p", [0, 17], 0), ("stress", [6, 7, 33], 0),
-    ("720p-dense", [0, 13], 0), ("720p", [0, 23], 256), ("stress", [7, 33], 256)])
+    ("720p-dense", [0, 13], 0), ("720p", [0, 23], 256), ("stress", [7, 33], 256),
+    ("1080p", [0, 17], 256)])
 def test_full_size_sampled(name, heads, row_block):
     """Sampled rows at full size: in the plan's own launch configuration (the
     one the benchmark times) and in the 8-wave one."""
